@@ -1,0 +1,51 @@
+// Combine: gather each token's k expert outputs and reduce them with the gate
+// weights in fp32, then add the shared expert's output.  "7.13 Serving
+// Mixture-of-Experts", "Expert Parallelism Mechanics" step 4 and the
+// moe_ep_layer listing (weighted scatter-add to the home token), written here
+// as a gather so every output element has one writer and a fixed summation
+// order (slot j = 0..k-1, then the shared term).
+#include "moe_kernels.h"
+
+namespace moe {
+
+template <int ACT>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  const int t = blockIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;  // first of 4 columns
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int e = threadIdx.x; e < p.E; e += 256) p.expert_count[e] = 0;  // ready for the next route
+  if (c >= p.d) return;
+  const int k = p.k;
+  const int* rows = p.row_of + (size_t)t * k;
+  const float* w = p.topk_w + (size_t)t * k;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.expert_out + (size_t)rows[j] * p.d + c);
+    const float wj = w[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+  }
+  if (p.shared_out) {
+    const f32x4_t s = *reinterpret_cast<const f32x4_t*>(p.shared_out + (size_t)t * p.d + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += s[i];
+  }
+  if constexpr (ACT == MOE_F32) {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.y) + (size_t)t * p.d + c) = acc;
+  } else {
+    const uint32_t lo = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+    const uint32_t hi = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + (size_t)t * p.d + c) = make_uint2(lo, hi);
+  }
+}
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
+  const dim3 grid(p.T, (p.d / 4 + 255) / 256), block(256);
+  if (p.act_dtype == MOE_F32)
+    hipLaunchKernelGGL(combine_kernel<MOE_F32>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<MOE_BF16>, grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

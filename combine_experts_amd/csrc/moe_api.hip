@@ -1,0 +1,317 @@
+// C ABI: argument checks, workspace carving and kernel launches.  No host
+// synchronisation, no allocation: every call only enqueues work on the
+// caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "moe_kernels.h"
+
+using namespace moe;
+
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  const int E = c->num_experts, k = c->top_k, G = c->n_group, kg = c->topk_group;
+  if (E < 1 || E > 1024 || k < 1 || k > 64 || k > E) return MOE_ERR_INVALID_ARG;
+  if (c->d_model <= 0 || c->d_ff <= 0) return MOE_ERR_INVALID_ARG;
+  if (c->num_shared != 0 && c->num_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (c->num_shared == 1 && c->d_ff_shared <= 0) return MOE_ERR_INVALID_ARG;
+  if (G < 1 || G > 64 || E % G != 0 || kg < 1 || kg > G) return MOE_ERR_INVALID_ARG;
+  if (k > kg * (E / G)) return MOE_ERR_INVALID_ARG;
+  if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c->weight_fn != MOE_WEIGHT_NORM_SUM && c->weight_fn != MOE_WEIGHT_SOFTMAX_SELECTED) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(c->routed_scale)) return MOE_ERR_INVALID_ARG;
+  const int a = c->act_dtype, w = c->weight_dtype;
+  if (a < MOE_F32 || a > MOE_FP8_E4M3 || w < MOE_F32 || w > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const bool combo = (a == MOE_F32 && w == MOE_F32) || (a == MOE_BF16 && w == MOE_BF16) ||
+                     (a == MOE_BF16 && w == MOE_FP8_E4M3);
+  if (!combo) return MOE_ERR_UNSUPPORTED;
+  const int mult = w == MOE_F32 ? 64 : w == MOE_BF16 ? 128 : 256;
+  if (c->d_model % mult || c->d_ff % mult) return MOE_ERR_UNSUPPORTED;
+  if (c->num_shared && c->d_ff_shared % mult) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool fp8(const moe_config* c) { return c->weight_dtype == MOE_FP8_E4M3; }
+
+// dtype of the dispatch buffer rows and of the SwiGLU activations
+int recv_dtype(const moe_config* c) { return fp8(c) ? MOE_FP8_E4M3 : c->act_dtype; }
+
+int64_t dispatch_rows(const moe_config* c, int64_t T) {
+  return T * c->top_k + ((fp8(c) && c->num_shared) ? T : 0);
+}
+
+struct FfnLayout {
+  size_t h, h_scale, hs, hs_scale, total;
+};
+
+FfnLayout ffn_layout(const moe_config* c, int64_t T) {
+  FfnLayout L{};
+  const size_t eb = elem_bytes(recv_dtype(c));
+  const size_t rows = (size_t)T * c->top_k;
+  size_t o = 0;
+  L.h = o;
+  o = align256(o + rows * c->d_ff * eb);
+  L.h_scale = o;
+  if (fp8(c)) o = align256(o + rows * (c->d_ff / 128) * sizeof(float));
+  L.hs = o;
+  if (c->num_shared) o = align256(o + (size_t)T * c->d_ff_shared * eb);
+  L.hs_scale = o;
+  if (c->num_shared && fp8(c)) o = align256(o + (size_t)T * (c->d_ff_shared / 128) * sizeof(float));
+  L.total = o;
+  return L;
+}
+
+struct LayerLayout {
+  size_t count, idx, w, ticket, row_of, offset, recv, recv_scale, eout, sout, ffn, total;
+};
+
+// expert_count sits at offset 0 for every T, so the zero invariant that
+// moe_combine restores carries over between calls of any size.
+LayerLayout layer_layout(const moe_config* c, int64_t T) {
+  LayerLayout L{};
+  const size_t tk = (size_t)T * c->top_k, d = c->d_model;
+  const size_t rows = (size_t)dispatch_rows(c, T);
+  size_t o = 0;
+  L.count = o;  o = align256(o + (size_t)c->num_experts * 4);
+  L.idx = o;    o = align256(o + tk * 4);
+  L.w = o;      o = align256(o + tk * 4);
+  L.ticket = o; o = align256(o + tk * 4);
+  L.row_of = o; o = align256(o + tk * 4);
+  L.offset = o; o = align256(o + (size_t)(c->num_experts + 1) * 4);
+  L.recv = o;   o = align256(o + rows * d * elem_bytes(recv_dtype(c)));
+  L.recv_scale = o;
+  if (fp8(c)) o = align256(o + rows * (d / 128) * sizeof(float));
+  L.eout = o;   o = align256(o + tk * d * sizeof(float));
+  L.sout = o;
+  if (c->num_shared) o = align256(o + (size_t)T * d * sizeof(float));
+  L.ffn = o;    o = align256(o + ffn_layout(c, T).total);
+  L.total = o;
+  return L;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+template <typename... P>
+bool all_aligned(P... ps) { return (aligned16(ps) && ...); }
+
+moe_status route_impl(const moe_config* c, int32_t T, const float* logits, const float* bias, int32_t* idx,
+                      float* w, int32_t* count, int32_t* ticket, hipStream_t s) {
+  RouteParams p{};
+  p.T = T; p.E = c->num_experts; p.k = c->top_k; p.n_group = c->n_group; p.topk_group = c->topk_group;
+  p.score_fn = c->score_fn; p.weight_fn = c->weight_fn; p.routed_scale = c->routed_scale;
+  p.logits = logits; p.bias = bias; p.topk_idx = idx; p.topk_w = w; p.expert_count = count; p.ticket = ticket;
+  return hip_status(launch_route(p, s));
+}
+
+moe_status dispatch_impl(const moe_config* c, int32_t T, const void* x, const int32_t* idx, const int32_t* count,
+                         const int32_t* ticket, void* recv, float* recv_scale, int32_t* offset, int32_t* row_of,
+                         hipStream_t s) {
+  DispatchParams p{};
+  p.T = T; p.E = c->num_experts; p.k = c->top_k; p.d = c->d_model; p.act_dtype = c->act_dtype;
+  p.quant = fp8(c) ? 1 : 0;
+  p.shared_rows = (fp8(c) && c->num_shared) ? 1 : 0;
+  p.x = x; p.topk_idx = idx; p.expert_count = count; p.ticket = ticket; p.recv = recv; p.recv_scale = recv_scale;
+  p.expert_offset = offset; p.row_of = row_of;
+  return hip_status(launch_dispatch(p, s));
+}
+
+moe_status ffn_impl(const moe_config* c, int32_t T, const void* recv, const float* recv_scale,
+                    const int32_t* offset, const moe_weights* W, const void* x, float* eout, float* sout,
+                    void* ws, hipStream_t s) {
+  const FfnLayout L = ffn_layout(c, T);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const int wdt = c->weight_dtype;
+  const int hdt = recv_dtype(c);
+  const int E = c->num_experts, d = c->d_model, F = c->d_ff, Fs = c->d_ff_shared;
+  const int ns = c->num_shared;
+  const int max_groups = (int)(((int64_t)T * c->top_k) < E ? (int64_t)T * c->top_k : E);
+  const int max_rows = T;  // no expert takes a token twice; the shared expert takes all T
+  const bool q = fp8(c);
+
+  // pass 1: gate/up + SwiGLU -> h
+  FfnParams a{};
+  a.E = E; a.T = T; a.expert_offset = offset; a.n_shared = ns;
+  const int tc1 = ffn_tile_cols(wdt, true);
+  a.tiles_r = F / tc1; a.tiles_s = ns ? Fs / tc1 : 0;
+  a.act = static_cast<const uint8_t*>(recv); a.act_scale = recv_scale;
+  a.w = static_cast<const uint8_t*>(W->w13); a.w_scale = W->w13_scale;
+  a.K_r = d; a.NW_r = 2 * F; a.Nout_r = F;
+  a.out = base + L.h; a.out_scale = q ? reinterpret_cast<float*>(base + L.h_scale) : nullptr;
+  if (ns) {
+    if (q) {
+      a.s_act = static_cast<const uint8_t*>(recv) + (size_t)T * c->top_k * d;
+      a.s_act_scale = recv_scale + (size_t)T * c->top_k * (d / 128);
+    } else {
+      a.s_act = static_cast<const uint8_t*>(x);
+    }
+    a.s_w = static_cast<const uint8_t*>(W->ws13); a.s_w_scale = W->ws13_scale;
+    a.K_s = d; a.NW_s = 2 * Fs; a.Nout_s = Fs;
+    a.s_out = base + L.hs; a.s_out_scale = q ? reinterpret_cast<float*>(base + L.hs_scale) : nullptr;
+  }
+  moe_status st = hip_status(launch_ffn(a, wdt, true, hdt, max_rows, max_groups, s));
+  if (st != MOE_OK) return st;
+
+  // pass 2: down projection -> expert_out / shared_out (fp32)
+  FfnParams b{};
+  b.E = E; b.T = T; b.expert_offset = offset; b.n_shared = ns;
+  const int tc2 = ffn_tile_cols(wdt, false);
+  b.tiles_r = d / tc2; b.tiles_s = ns ? d / tc2 : 0;
+  b.act = base + L.h; b.act_scale = q ? reinterpret_cast<const float*>(base + L.h_scale) : nullptr;
+  b.w = static_cast<const uint8_t*>(W->w2); b.w_scale = W->w2_scale;
+  b.K_r = F; b.NW_r = d; b.Nout_r = d;
+  b.out = eout;
+  if (ns) {
+    b.s_act = base + L.hs; b.s_act_scale = q ? reinterpret_cast<const float*>(base + L.hs_scale) : nullptr;
+    b.s_w = static_cast<const uint8_t*>(W->ws2); b.s_w_scale = W->ws2_scale;
+    b.K_s = Fs; b.NW_s = d; b.Nout_s = d;
+    b.s_out = sout;
+  }
+  return hip_status(launch_ffn(b, wdt, false, MOE_F32, max_rows, max_groups, s));
+}
+
+moe_status combine_impl(const moe_config* c, int32_t T, const float* eout, const int32_t* row_of,
+                        const float* w, const float* sout, void* y, int32_t* count, hipStream_t s) {
+  CombineParams p{};
+  p.T = T; p.E = c->num_experts; p.k = c->top_k; p.d = c->d_model; p.act_dtype = c->act_dtype;
+  p.expert_out = eout; p.row_of = row_of; p.topk_w = w; p.shared_out = sout; p.y = y; p.expert_count = count;
+  return hip_status(launch_combine(p, s));
+}
+
+moe_status check_weights(const moe_config* c, const moe_weights* W) {
+  if (!W || !W->w13 || !W->w2) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(W->w13, W->w2)) return MOE_ERR_INVALID_ARG;
+  if (c->num_shared && (!W->ws13 || !W->ws2 || !all_aligned(W->ws13, W->ws2))) return MOE_ERR_INVALID_ARG;
+  if (fp8(c)) {
+    if (!W->w13_scale || !W->w2_scale) return MOE_ERR_INVALID_ARG;
+    if (c->num_shared && (!W->ws13_scale || !W->ws2_scale)) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_dispatch_rows(const moe_config* cfg, int32_t T) {
+  if (check_config(cfg) != MOE_OK || T < 0) return -1;
+  return dispatch_rows(cfg, T);
+}
+
+size_t moe_ffn_workspace_size(const moe_config* cfg, int32_t max_tokens) {
+  if (check_config(cfg) != MOE_OK || max_tokens < 0) return 0;
+  return ffn_layout(cfg, max_tokens).total;
+}
+
+size_t moe_workspace_size(const moe_config* cfg, int32_t max_tokens) {
+  if (check_config(cfg) != MOE_OK || max_tokens < 0) return 0;
+  return layer_layout(cfg, max_tokens).total;
+}
+
+moe_status moe_route(const moe_config* cfg, int32_t T, const float* logits, const float* bias, int32_t* topk_idx,
+                     float* topk_w, int32_t* expert_count, int32_t* ticket, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w || !expert_count || !ticket) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(logits, topk_idx, topk_w, expert_count, ticket) || (bias && !aligned16(bias)))
+    return MOE_ERR_INVALID_ARG;
+  return route_impl(cfg, T, logits, bias, topk_idx, topk_w, expert_count, ticket, (hipStream_t)stream);
+}
+
+moe_status moe_dispatch(const moe_config* cfg, int32_t T, const void* x, const int32_t* topk_idx,
+                        const int32_t* expert_count, const int32_t* ticket, void* recv, float* recv_scale,
+                        int32_t* expert_offset, int32_t* row_of, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !topk_idx || !expert_count || !ticket || !recv || !expert_offset || !row_of) return MOE_ERR_INVALID_ARG;
+  if (fp8(cfg) && !recv_scale) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(x, topk_idx, expert_count, ticket, recv, expert_offset, row_of)) return MOE_ERR_INVALID_ARG;
+  if (recv_scale && !aligned16(recv_scale)) return MOE_ERR_INVALID_ARG;
+  return dispatch_impl(cfg, T, x, topk_idx, expert_count, ticket, recv, recv_scale, expert_offset, row_of,
+                       (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t T, const void* recv, const float* recv_scale,
+                          const int32_t* expert_offset, const moe_weights* w, const void* x, float* expert_out,
+                          float* shared_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if ((st = check_weights(cfg, w)) != MOE_OK) return st;
+  if (!recv || !expert_offset || !expert_out || !ws) return MOE_ERR_INVALID_ARG;
+  if (fp8(cfg) && !recv_scale) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared && (!shared_out || (!fp8(cfg) && !x))) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(recv, expert_offset, expert_out, ws)) return MOE_ERR_INVALID_ARG;
+  if ((recv_scale && !aligned16(recv_scale)) || (x && !aligned16(x)) || (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_layout(cfg, T).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return ffn_impl(cfg, T, recv, recv_scale, expert_offset, w, x, expert_out, shared_out, ws, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out, const int32_t* row_of,
+                       const float* topk_w, const float* shared_out, void* y, int32_t* expert_count,
+                       void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!expert_out || !row_of || !topk_w || !y || !expert_count) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(expert_out, row_of, topk_w, y, expert_count) || (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARG;
+  return combine_impl(cfg, T, expert_out, row_of, topk_w, shared_out, y, expert_count, (hipStream_t)stream);
+}
+
+moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const float* logits, const float* bias,
+                     const moe_weights* w, void* y, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if ((st = check_weights(cfg, w)) != MOE_OK) return st;
+  if (!x || !logits || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(x, logits, y, ws) || (bias && !aligned16(bias))) return MOE_ERR_INVALID_ARG;
+  const LayerLayout L = layer_layout(cfg, T);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  int32_t* count = reinterpret_cast<int32_t*>(b + L.count);
+  int32_t* idx = reinterpret_cast<int32_t*>(b + L.idx);
+  float* tw = reinterpret_cast<float*>(b + L.w);
+  int32_t* ticket = reinterpret_cast<int32_t*>(b + L.ticket);
+  int32_t* row_of = reinterpret_cast<int32_t*>(b + L.row_of);
+  int32_t* offset = reinterpret_cast<int32_t*>(b + L.offset);
+  void* recv = b + L.recv;
+  float* recv_scale = fp8(cfg) ? reinterpret_cast<float*>(b + L.recv_scale) : nullptr;
+  float* eout = reinterpret_cast<float*>(b + L.eout);
+  float* sout = cfg->num_shared ? reinterpret_cast<float*>(b + L.sout) : nullptr;
+  void* ffn_ws = b + L.ffn;
+  if ((st = route_impl(cfg, T, logits, bias, idx, tw, count, ticket, s)) != MOE_OK) return st;
+  if ((st = dispatch_impl(cfg, T, x, idx, count, ticket, recv, recv_scale, offset, row_of, s)) != MOE_OK) return st;
+  if ((st = ffn_impl(cfg, T, recv, recv_scale, offset, w, x, eout, sout, ffn_ws, s)) != MOE_OK) return st;
+  return combine_impl(cfg, T, eout, row_of, tw, sout, y, count, s);
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: configuration not supported by the kernels";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace below the required size";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown moe_status";
+}
+
+}  // extern "C"

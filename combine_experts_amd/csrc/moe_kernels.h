@@ -1,0 +1,85 @@
+// Kernel parameter blocks and launchers (internal to the library).
+#pragma once
+
+#include "moe_device.h"
+
+namespace moe {
+
+struct RouteParams {
+  int T, E, k, n_group, topk_group, score_fn, weight_fn;
+  float routed_scale;
+  const float* logits;
+  const float* bias;
+  int* topk_idx;
+  float* topk_w;
+  int* expert_count;
+  int* ticket;
+};
+
+struct DispatchParams {
+  int T, E, k, d, act_dtype;
+  int quant;        // write E4M3 codes + per-128 scales
+  int shared_rows;  // also write rows T*k + t for the shared expert (quant only)
+  const void* x;
+  const int* topk_idx;
+  const int* expert_count;
+  const int* ticket;
+  void* recv;
+  float* recv_scale;
+  int* expert_offset;
+  int* row_of;
+};
+
+// One grouped GEMM pass over the dispatch layout.  Work item = (group, tile):
+// groups are the experts with rows (ranked by index) and then the shared
+// expert; a tile is 16*FW consecutive output columns.  GATED passes multiply
+// the gate rows [c, c+16FW) and the up rows [Nout + c, ...) of the same
+// weight matrix and write silu(gate) * up; plain passes write the product.
+struct FfnParams {
+  int E, T;
+  const int* expert_offset;  // [E+1]
+  int n_shared;
+  int tiles_r, tiles_s;
+  // routed experts: activation rows [expert_offset[e], expert_offset[e+1])
+  const uint8_t* act;
+  const float* act_scale;  // E4M3 only: [rows][K_r/128]
+  const uint8_t* w;        // [E][NW_r][K_r]
+  const float* w_scale;    // E4M3 only: [E][NW_r/128][K_r/128]
+  int K_r, NW_r, Nout_r;
+  void* out;               // [rows][Nout_r]
+  float* out_scale;        // E4M3 output only: [rows][Nout_r/128]
+  // shared expert: activation rows [0, T)
+  const uint8_t* s_act;
+  const float* s_act_scale;
+  const uint8_t* s_w;
+  const float* s_w_scale;
+  int K_s, NW_s, Nout_s;
+  void* s_out;
+  float* s_out_scale;
+};
+
+struct CombineParams {
+  int T, E, k, d, act_dtype;
+  const float* expert_out;
+  const int* row_of;
+  const float* topk_w;
+  const float* shared_out;
+  void* y;
+  int* expert_count;
+};
+
+hipError_t launch_route(const RouteParams& p, hipStream_t stream);
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream);
+// gated: gate/up + SwiGLU pass; otherwise the down pass.  max_rows bounds the
+// rows of any group (T for the shared expert).
+hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, int out_dtype, int max_rows,
+                      int max_groups, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+// Work-partition constants of the grouped GEMMs, also used by the host to size
+// the grid: a gated E4M3 pass covers 128 output columns per item (so each
+// 1x128 activation block is quantised inside one workgroup); every other pass
+// covers 16.
+inline int ffn_tile_cols(int wdtype, bool gated) { return (gated && wdtype == MOE_FP8_E4M3) ? 128 : 16; }
+
+}  // namespace moe

@@ -1,0 +1,310 @@
+// Router and one-sided dispatch kernels.
+//
+// Router: "Mixture-of-experts serving" (learn-kernels) paragraph 1 (sigmoid
+// affinity + per-expert bias that steers selection), paragraph 4
+// (group-limited routing); "7.13 Serving Mixture-of-Experts", moe_ep_layer
+// listing (softmax, top-k, renormalise).  Dispatch: "One-Sided
+// Expert-Parallel All-to-All ... over NVLink" (abstract): tokens are pushed
+// without a metadata exchange into expert-grouped buffers read in place; a
+// token reserves its slot with an atomic add on its expert's counter.
+#include "moe_kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Router: one wavefront per token.  Lane l holds experts l*KPL .. l*KPL+KPL-1.
+// ---------------------------------------------------------------------------
+
+// Total order of candidates: larger key first, then lower index.
+__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+template <int KPL>
+__global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
+  extern __shared__ float smem[];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wid;
+  const int E = p.E;
+  // per-wave LDS: keys[E], scores[E], group scores[64], group chosen[64]
+  float* kbuf = smem + wid * (2 * E + 128);
+  float* sbuf = kbuf + E;
+  float* gbuf = sbuf + E;
+  float* cbuf = gbuf + 64;
+  if (t >= p.T) return;  // uniform per wave; no block barrier is used below
+
+  const float* lg = p.logits + (size_t)t * E;
+  float key[KPL];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane * KPL + i;
+    float k = -INFINITY, s = 0.f;
+    if (e < E) {
+      const float l = lg[e];
+      if (p.score_fn == MOE_SCORE_SIGMOID) {
+        // sigmoid evaluated in double and rounded once to fp32
+        s = (float)(1.0 / (1.0 + exp(-(double)l)));
+        k = p.bias ? s + p.bias[e] : s;
+      } else {
+        s = l;
+        k = l;
+        if (l == l) lmax = fmaxf(lmax, l);
+      }
+      if (k != k) k = -INFINITY;
+      kbuf[e] = k;
+      sbuf[e] = s;
+    }
+    key[i] = k;
+  }
+
+  // ---- group stage: lane q < G scores group q; the kg best groups survive
+  const int G = p.n_group;
+  const int gsize = E / G;
+  bool elig[KPL];
+  if (G > 1) {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    if (lane < G) {
+      float b1 = -INFINITY, b2 = -INFINITY;
+      for (int j = 0; j < gsize; ++j) {
+        const float v = kbuf[lane * gsize + j];
+        if (v > b1) { b2 = b1; b1 = v; }
+        else if (v > b2) b2 = v;
+      }
+      float gs = gsize == 1 ? b1 : b1 + b2;
+      if (gs != gs) gs = -INFINITY;
+      gbuf[lane] = gs;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane < G) {
+      const float mine = gbuf[lane];
+      int rank = 0;
+      for (int q = 0; q < G; ++q) rank += better(gbuf[q], q, mine, lane) ? 1 : 0;
+      cbuf[lane] = rank < p.topk_group ? 1.f : 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int e = lane * KPL + i;
+      elig[i] = e < E && cbuf[e / gsize] != 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) elig[i] = lane * KPL + i < E;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // ---- top-k: k rounds of a wave-wide arg-max on (key desc, index asc)
+  int my_idx = 0;
+  float my_s = 0.f;
+  for (int r = 0; r < p.k; ++r) {
+    float bk = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int e = lane * KPL + i;
+      if (elig[i] && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ok = __shfl_xor(bk, off);
+      const int oi = __shfl_xor(bi, off);
+      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
+    }
+    // Validation guarantees at least k eligible experts, so a winner always
+    // exists; the clamp only keeps every later index in range regardless.
+    if (bi >= E) bi = 0;
+    // every lane now holds the same winner; its owner retires it
+    if (bi / KPL == lane) {
+#pragma unroll
+      for (int i = 0; i < KPL; ++i)
+        if (lane * KPL + i == bi) elig[i] = false;
+    }
+    if (lane == r) {
+      my_idx = bi;
+      my_s = sbuf[bi];
+    }
+  }
+
+  // ---- gate weights from the unbiased scores of the k chosen experts
+  const int k = p.k;
+  float w = 0.f;
+  if (p.score_fn == MOE_SCORE_SOFTMAX) {
+    // p_e = exp(l_e - M) / Z over all experts
+    float m = lmax;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (p.weight_fn == MOE_WEIGHT_NORM_SUM) {
+      // p_j / sum p over the chosen = exp(l_j - M) / sum exp(l_i - M)
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += expf(__shfl(my_s, j) - m);
+      w = expf(my_s - m) / den;
+    } else {
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int e = lane * KPL + i;
+        if (e < E) z += expf(sbuf[e] - m);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+      const float pj = expf(my_s - m) / z;
+      float pm = -INFINITY;
+      for (int j = 0; j < k; ++j) pm = fmaxf(pm, __shfl(pj, j));
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += expf(__shfl(pj, j) - pm);
+      w = expf(pj - pm) / den;
+    }
+  } else {
+    if (p.weight_fn == MOE_WEIGHT_NORM_SUM) {
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += __shfl(my_s, j);
+      w = my_s / den;
+    } else {
+      float sm = -INFINITY;
+      for (int j = 0; j < k; ++j) sm = fmaxf(sm, __shfl(my_s, j));
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += expf(__shfl(my_s, j) - sm);
+      w = expf(my_s - sm) / den;
+    }
+  }
+  w *= p.routed_scale;
+
+  if (lane < k) {
+    const size_t o = (size_t)t * k + lane;
+    p.topk_idx[o] = my_idx;
+    p.topk_w[o] = w;
+    p.ticket[o] = atomicAdd(p.expert_count + my_idx, 1);
+  }
+}
+
+hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
+  const int kpl_needed = (p.E + 63) / 64;
+  const int blocks = (p.T + 3) / 4;
+  const size_t lds = 4 * (2 * (size_t)p.E + 128) * sizeof(float);
+#define MOE_ROUTE_CASE(K)                                                                \
+  if (kpl_needed <= K) {                                                                 \
+    hipLaunchKernelGGL(route_kernel<K>, dim3(blocks), dim3(256), lds, stream, p);        \
+    return hipGetLastError();                                                            \
+  }
+  MOE_ROUTE_CASE(1)
+  MOE_ROUTE_CASE(2)
+  MOE_ROUTE_CASE(4)
+  MOE_ROUTE_CASE(8)
+  MOE_ROUTE_CASE(16)
+#undef MOE_ROUTE_CASE
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch: one block per token.  Every block recomputes the exclusive scan of
+// the expert counters in LDS (no separate count pass), then writes its token
+// into the rows it reserved.
+// ---------------------------------------------------------------------------
+
+// Exclusive prefix sum of cnt[0..E) into off[0..E] (LDS), 256 threads, E <= 1024.
+__device__ void block_offsets(const int* cnt, int E, int* off, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int v[4];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    v[i] = e < E ? cnt[e] : 0;
+    local += v[i];
+  }
+  // inclusive scan of `local` across the wave
+  int inc = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wid] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += wsum[w];
+  int run = base + inc - local;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) off[e] = run;
+    run += v[i];
+  }
+  if (tid == 255) off[E] = run;  // E <= 1024 = 256 * 4, so thread 255 ends the scan
+  __syncthreads();
+}
+
+template <int ACT, bool QUANT>
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
+  __shared__ int off[1025];
+  __shared__ int wsum[4];
+  __shared__ int rows[65];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  block_offsets(p.expert_count, p.E, off, wsum);
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= p.E; e += 256) p.expert_offset[e] = off[e];
+  const int k = p.k;
+  if (tid < k) {
+    const size_t o = (size_t)t * k + tid;
+    const int r = off[p.topk_idx[o]] + p.ticket[o];
+    rows[tid] = r;
+    p.row_of[o] = r;
+  }
+  if (tid == 0) rows[k] = QUANT && p.shared_rows ? k * p.T + t : -1;
+  __syncthreads();
+  const int d = p.d;
+  const int nrows = (QUANT && p.shared_rows) ? k + 1 : k;
+
+  if constexpr (!QUANT) {
+    // plain copy, 16-byte pieces
+    constexpr int EB = Elem<ACT>::kBytes;
+    const int pieces = d * EB / 16;
+    const i32x4_t* src = reinterpret_cast<const i32x4_t*>(static_cast<const uint8_t*>(p.x) + (size_t)t * d * EB);
+    for (int c = tid; c < pieces; c += 256) {
+      const i32x4_t v = src[c];
+      for (int j = 0; j < nrows; ++j)
+        reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d * EB)[c] = v;
+    }
+  } else {
+    // E4M3 per 128 columns: one wave per 128-column block, 2 columns per lane
+    const int lane = tid & 63, wid = tid >> 6;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.x) + (size_t)t * d);
+    const int nb = d / 128;
+    for (int b = wid; b < nb; b += 4) {
+      const uint32_t pair = src[b * 64 + lane];
+      const float v0 = bf16_bits_to_f32(pair & 0xFFFFu), v1 = bf16_bits_to_f32(pair >> 16);
+      float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+      const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+      const uint32_t c0 = f32_to_e4m3(v0 / scale), c1 = f32_to_e4m3(v1 / scale);
+      const uint16_t codes = (uint16_t)(c0 | (c1 << 8));
+      for (int j = 0; j < nrows; ++j) {
+        uint8_t* dst = static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d;
+        reinterpret_cast<uint16_t*>(dst + b * 128)[lane] = codes;
+        if (lane == 0) p.recv_scale[(size_t)rows[j] * nb + b] = scale;
+      }
+    }
+  }
+}
+
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream) {
+  dim3 grid(p.T), block(256);
+  if (p.quant) {
+    hipLaunchKernelGGL((dispatch_kernel<MOE_BF16, true>), grid, block, 0, stream, p);
+  } else if (p.act_dtype == MOE_F32) {
+    hipLaunchKernelGGL((dispatch_kernel<MOE_F32, false>), grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((dispatch_kernel<MOE_BF16, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,229 @@
+/*
+ * moe.h - C ABI of one GPU's share of an expert-parallel Mixture-of-Experts
+ * layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (sources named by page title and section):
+ *   route     "Mixture-of-experts serving" (learn-kernels), paragraph 1:
+ *             sigmoid affinity per expert plus a per-expert bias that only
+ *             steers selection; paragraph 4: group-limited routing.
+ *             "7.13 Serving Mixture-of-Experts" (llm-stack-book), section
+ *             "Expert Parallelism Mechanics", the moe_ep_layer listing:
+ *             softmax, top-k, renormalise the chosen k.
+ *   dispatch  same chapter, mechanics step 2 (rows of one expert made
+ *             contiguous), and "One-Sided Expert-Parallel All-to-All for
+ *             Mixture-of-Experts Inference over NVLink" (abstract): each
+ *             token is pushed without a metadata exchange into expert-grouped
+ *             buffers that the grouped GEMMs read in place.  Here a token
+ *             reserves its slot with a per-expert atomic counter.
+ *             "DeepEP" section, trick 1: activations quantised to E4M3.
+ *   expert    mechanics step 3: one grouped GEMM over all local experts;
+ *   ffn       the experts are SwiGLU FFNs, plus the always-on shared expert
+ *             ("Hot-Expert Skew" section, "Shared experts as a relief
+ *             valve"; learn-kernels paragraph 1).
+ *   combine   mechanics step 4 and the moe_ep_layer listing: weighted sum of
+ *             each token's k expert outputs, plus the shared expert's output
+ *             (DeepEP decode sketch: combine(...) + shared_out).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is device memory owned by the caller, except
+ *     the moe_config / moe_weights structs themselves, which are host memory
+ *     read during the call only.  The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and is asynchronous.
+ *   - Arguments are checked before anything is launched; a failed check
+ *     returns its status and launches nothing.  A failed launch returns
+ *     MOE_ERR_HIP.  There is no device-side error reporting.
+ *   - T = 0 is valid and launches nothing.
+ *   - Row-major layouts throughout; "K-contiguous" means the reduction index
+ *     is the fastest-varying one.  Device pointers must be 16-byte aligned.
+ *   - Element types: MOE_F32 = IEEE binary32, MOE_BF16 = bfloat16 bit
+ *     patterns (uint16), MOE_FP8_E4M3 = OCP E4M3FN bytes (max 448, no inf).
+ *   - The library holds no mutable global state: calls on different streams
+ *     with different buffers may run concurrently.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,         /* null/misaligned pointer, bad size or config */
+  MOE_ERR_UNSUPPORTED = 2,         /* valid config outside what the kernels cover */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the matching *_workspace_size */
+  MOE_ERR_HIP = 4                  /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+typedef enum {
+  MOE_WEIGHT_NORM_SUM = 0,        /* w_j = s_j / sum_i s_i over the chosen k      */
+  MOE_WEIGHT_SOFTMAX_SELECTED = 1 /* w_j = exp(s_j) / sum_i exp(s_i) over the k   */
+} moe_weight_fn;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/*
+ * Layer shape and routing rule.
+ *   num_experts E (1..1024), top_k k (1..64, k <= topk_group * E / n_group),
+ *   d_model d, d_ff F (routed experts), num_shared (0 or 1), d_ff_shared Fs.
+ *   n_group G (1..64, divides E), topk_group kg (1..G):
+ *     experts form G contiguous groups of E/G; a group's score is the sum of
+ *     its two largest selection keys (its only key when E/G = 1); the kg best
+ *     groups are kept and the top k are chosen among their experts.  G = 1
+ *     is plain top-k.
+ *   score_fn: SIGMOID -> s_e = sigmoid(logit_e), key_e = s_e + bias_e (fp32);
+ *             SOFTMAX -> s = softmax(logits), key_e = logit_e (same order).
+ *   weight_fn: how the k weights are formed from the unbiased s of the chosen
+ *             experts; then every weight is multiplied by routed_scale.
+ *   Ties: lower group index, then lower expert index wins.  NaN keys count as
+ *   -inf.  topk_idx lists the k experts by descending key.
+ *   act_dtype (x and y): MOE_F32 or MOE_BF16.
+ *   weight_dtype: MOE_F32 (with act F32), MOE_BF16 (with act BF16) or
+ *   MOE_FP8_E4M3 (with act BF16: activations are quantised to E4M3 per
+ *   token per 128 columns inside the layer; weights carry 128x128 block
+ *   scales).
+ *   Size rules: d, F, Fs multiples of 64 (F32), 128 (BF16) or 256 (FP8).
+ */
+typedef struct {
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t num_shared;
+  int32_t d_ff_shared;
+  int32_t n_group;
+  int32_t topk_group;
+  int32_t score_fn;  /* moe_score_fn  */
+  int32_t weight_fn; /* moe_weight_fn */
+  float routed_scale;
+  int32_t act_dtype;    /* moe_dtype */
+  int32_t weight_dtype; /* moe_dtype */
+} moe_config;
+
+/*
+ * Expert weights (device memory, element type weight_dtype, K-contiguous):
+ *   w13  [E][2F][d]  rows [0, F) are the gate projection, rows [F, 2F) the up
+ *                    projection of each expert
+ *   w2   [E][d][F]   down projection
+ *   ws13 [2Fs][d], ws2 [d][Fs]  shared expert (NULL when num_shared == 0)
+ * FP8 only: fp32 scales per 128 x 128 block of each matrix,
+ *   w13_scale [E][2F/128][d/128], w2_scale [E][d/128][F/128],
+ *   ws13_scale [2Fs/128][d/128], ws2_scale [d/128][Fs/128];
+ *   the weight is code * scale.  Ignored (may be NULL) otherwise.
+ */
+typedef struct {
+  const void* w13;
+  const void* w2;
+  const void* ws13;
+  const void* ws2;
+  const float* w13_scale;
+  const float* w2_scale;
+  const float* ws13_scale;
+  const float* ws2_scale;
+} moe_weights;
+
+/* Row count of the dispatch buffer for T tokens: T*k routed rows, plus T rows
+ * holding the quantised tokens for the shared expert when weight_dtype is
+ * FP8 and num_shared is 1 (in the bf16 and f32 paths the shared expert reads
+ * x directly). */
+int64_t moe_dispatch_rows(const moe_config* cfg, int32_t T);
+
+/* Bytes of device workspace moe_expert_ffn needs for up to max_tokens tokens
+ * (0 on an invalid config or max_tokens < 0). */
+size_t moe_ffn_workspace_size(const moe_config* cfg, int32_t max_tokens);
+
+/* Bytes of device workspace moe_layer needs for up to max_tokens tokens
+ * (0 on an invalid config or max_tokens < 0).  The caller zero-fills the
+ * workspace once after allocating it; the layer leaves its counters at zero
+ * when it returns, so the same workspace serves every later call. */
+size_t moe_workspace_size(const moe_config* cfg, int32_t max_tokens);
+
+/*
+ * moe_route: scores, group-limited top-k, gate weights and slot tickets.
+ *   logits       [T][E] fp32
+ *   bias         [E] fp32, or NULL for no bias (used by SIGMOID only)
+ *   topk_idx     [T][k] int32 out: chosen experts, descending key
+ *   topk_w       [T][k] fp32 out: gate weights (sum = routed_scale)
+ *   expert_count [E] int32 in/out: MUST be zero on entry; on exit holds the
+ *                number of (token, slot) pairs routed to each expert
+ *   ticket       [T][k] int32 out: the token's slot within its expert's rows,
+ *                taken with an atomic add on expert_count; tickets of one
+ *                expert are a permutation of 0..count-1 in an unspecified
+ *                order
+ */
+moe_status moe_route(const moe_config* cfg, int32_t T, const float* logits, const float* bias,
+                     int32_t* topk_idx, float* topk_w, int32_t* expert_count, int32_t* ticket,
+                     void* stream);
+
+/*
+ * moe_dispatch: one-sided write of every token into its experts' rows.
+ *   x             [T][d] act_dtype
+ *   topk_idx, expert_count, ticket: as left by moe_route
+ *   recv          [moe_dispatch_rows][d] out: act_dtype, or E4M3 bytes when
+ *                 weight_dtype is FP8.  Expert e owns rows
+ *                 [expert_offset[e], expert_offset[e+1]); token t's slot j
+ *                 lands in row expert_offset[topk_idx[t][j]] + ticket[t][j].
+ *                 FP8 + shared expert: row T*k + t holds token t.
+ *   recv_scale    [moe_dispatch_rows][d/128] fp32 out (FP8 only, else NULL):
+ *                 per-row, per-128-column scale; code = E4M3(x / scale) with
+ *                 scale = amax / 448 (1 when amax = 0), nearest-even, saturating
+ *   expert_offset [E+1] int32 out: exclusive prefix sum of expert_count
+ *   row_of        [T][k] int32 out: the row of token t's slot j
+ */
+moe_status moe_dispatch(const moe_config* cfg, int32_t T, const void* x, const int32_t* topk_idx,
+                        const int32_t* expert_count, const int32_t* ticket, void* recv,
+                        float* recv_scale, int32_t* expert_offset, int32_t* row_of, void* stream);
+
+/*
+ * moe_expert_ffn: grouped SwiGLU experts over the dispatch buffer, read in
+ * place, and the shared expert over x.  Experts with no rows read none of
+ * their weights.
+ *   recv, recv_scale, expert_offset: as left by moe_dispatch
+ *   w            expert weights (host struct of device pointers)
+ *   x            [T][d] act_dtype (shared expert input; may be NULL when
+ *                num_shared == 0)
+ *   expert_out   [T*k][d] fp32 out: row r = W2 (silu(Wg a) * (Wu a)) for the
+ *                dispatch row a = recv[r]
+ *   shared_out   [T][d] fp32 out (NULL when num_shared == 0)
+ *   ws, ws_bytes device workspace of at least moe_ffn_workspace_size(cfg, T)
+ *                bytes (holds the SwiGLU activations between the two GEMMs)
+ */
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t T, const void* recv,
+                          const float* recv_scale, const int32_t* expert_offset,
+                          const moe_weights* w, const void* x, float* expert_out,
+                          float* shared_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine: y[t] = sum_j topk_w[t][j] * expert_out[row_of[t][j]]
+ * (accumulated in fp32 in slot order j = 0..k-1) + shared_out[t], rounded to
+ * act_dtype.  Also resets expert_count[0..E) to zero for the next call.
+ *   shared_out may be NULL (no shared term).  y is [T][d] act_dtype.
+ */
+moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out,
+                       const int32_t* row_of, const float* topk_w, const float* shared_out, void* y,
+                       int32_t* expert_count, void* stream);
+
+/*
+ * moe_layer: route -> dispatch -> expert FFN (+ shared expert) -> combine in
+ * one call, every intermediate carved from ws (>= moe_workspace_size(cfg, T)
+ * bytes, zero-filled once by the caller).  Launches only; no host sync, so
+ * the sequence can be captured in a HIP graph.
+ */
+moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const float* logits,
+                     const float* bias, const moe_weights* w, void* y, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -83,12 +83,18 @@ void gen_normal_bf16(uint64_t seed, uint64_t tensor_id, uint64_t offset, int64_t
     out[i] = f32_to_bf16_rne((float)(mean + std * normal_from_bits(draw(s, offset + (uint64_t)i))));
 }
 
-/* Value of non-negative E4M3FN code c (0..126): exponent bias 7, 3 mantissa
- * bits, subnormal step 2^-9, largest finite 448. */
-static double e4m3_value(int c) {
-  int e = (c >> 3) & 15, m = c & 7;
-  if (e == 0) return ldexp((double)m, -9);
-  return ldexp(1.0 + m / 8.0, e - 7);
+/* Values of the non-negative finite E4M3FN codes 0..126: exponent bias 7,
+ * 3 mantissa bits, subnormal step 2^-9, largest finite 448. */
+static double e4m3_table[127];
+static int e4m3_table_ready = 0;
+
+static void e4m3_table_init(void) {
+  if (e4m3_table_ready) return;
+  for (int c = 0; c < 127; ++c) {
+    int e = (c >> 3) & 15, m = c & 7;
+    e4m3_table[c] = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+  }
+  e4m3_table_ready = 1;
 }
 
 static uint8_t e4m3_encode_nearest(float v) {
@@ -96,12 +102,12 @@ static uint8_t e4m3_encode_nearest(float v) {
   double a = (double)v;
   if (a < 0) { sign = 0x80; a = -a; }
   if (a >= 448.0) return sign | 0x7E;
-  int lo = 0, hi = 126; /* value(lo) <= a < value(hi) holds after the loop */
+  int lo = 0, hi = 126; /* table[lo] <= a < table[hi] */
   while (hi - lo > 1) {
     int mid = (lo + hi) / 2;
-    if (e4m3_value(mid) <= a) lo = mid; else hi = mid;
+    if (e4m3_table[mid] <= a) lo = mid; else hi = mid;
   }
-  double dl = a - e4m3_value(lo), dh = e4m3_value(hi) - a;
+  double dl = a - e4m3_table[lo], dh = e4m3_table[hi] - a;
   int c;
   if (dl < dh) c = lo;
   else if (dh < dl) c = hi;
@@ -120,6 +126,7 @@ void gen_fp8_blocks(uint64_t seed, uint64_t tensor_id, uint64_t offset, int64_t 
                     double mean, double std, uint8_t* codes, float* scales) {
   uint64_t s = stream_state(seed, tensor_id);
   int64_t rb = rows / 128, cb = cols / 128;
+  e4m3_table_init();
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t b = 0; b < rb * cb; ++b) {
     int64_t br = b / cb, bc = b % cb;

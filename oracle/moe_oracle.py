@@ -53,7 +53,9 @@ Readings where the pages are silent (each also listed in the design notes):
   * fp8 (E4M3FN, max 448): per-token per-128-column activation scales
     amax/448 in fp32 (1 when amax = 0), code = nearest E4M3 value of x/scale
     in fp32 with ties to even, saturating at +-448.  Weights arrive as codes
-    plus 128x128 block scales and mean code * scale.
+    plus 128x128 block scales and mean code * scale.  The fp8 layer
+    quantises the rows entering both GEMMs (x, and h rounded to fp32) and
+    otherwise computes in float64.
 """
 from __future__ import annotations
 
@@ -257,19 +259,29 @@ def silu(z):
     return z * sigmoid(z)
 
 
-def swiglu_expert(a, w13, w2):
+def swiglu_expert(a, w13, w2, act_quant=False):
     """One expert on rows a [n][d]: w13 [2F][d] holds gate rows [0, F) and up
-    rows [F, 2F); w2 is [d][F].  out = (silu(a Wg^T) * (a Wu^T)) W2^T."""
+    rows [F, 2F); w2 is [d][F].  out = (silu(a Wg^T) * (a Wu^T)) W2^T.
+
+    act_quant: the E4M3 form of the layer ("DeepEP" section, trick 1): the
+    rows entering each GEMM are first quantised per 1x128 block (the input
+    rows as fp32, h after rounding to fp32) and the GEMM reads their
+    dequantised values code * scale."""
     a = np.asarray(a, dtype=np.float64)
     w13 = np.asarray(w13, dtype=np.float64)
     w2 = np.asarray(w2, dtype=np.float64)
     F = w13.shape[0] // 2
+    if act_quant:
+        a = dequant_rows_1x128(*quantize_rows_1x128(a.astype(np.float32)))
     gate = a @ w13[:F].T
     up = a @ w13[F:].T
-    return (silu(gate) * up) @ w2.T
+    h = silu(gate) * up
+    if act_quant:
+        h = dequant_rows_1x128(*quantize_rows_1x128(h.astype(np.float32)))
+    return h @ w2.T
 
 
-def expert_ffn(recv, offsets, get_expert):
+def expert_ffn(recv, offsets, get_expert, act_quant=False):
     """Grouped expert compute over the dispatched rows ([P2] step 3: one
     matmul per expert); get_expert(e) -> (w13, w2) as float64."""
     recv = np.asarray(recv, dtype=np.float64)
@@ -280,14 +292,14 @@ def expert_ffn(recv, offsets, get_expert):
         if hi == lo:
             continue
         w13, w2 = get_expert(e)
-        o = swiglu_expert(recv[lo:hi], w13, w2)
+        o = swiglu_expert(recv[lo:hi], w13, w2, act_quant)
         if out is None:
             out = np.zeros((recv.shape[0], o.shape[1]), dtype=np.float64)
         out[lo:hi] = o
     return out
 
 
-def layer(x, logits, bias, spec, get_expert, get_shared=None, idx=None, w=None):
+def layer(x, logits, bias, spec, get_expert, get_shared=None, idx=None, w=None, act_quant=False):
     """The whole layer, step by step: route, dispatch, expert FFN, shared
     expert, combine.  Passing idx and w evaluates the layer under a given
     routing (used where a near-tie legitimately flips a choice)."""
@@ -296,34 +308,37 @@ def layer(x, logits, bias, spec, get_expert, get_shared=None, idx=None, w=None):
         idx, w, _ = route(logits, bias, spec)
     counts, offsets, row_of, token_of_row = dispatch(idx, spec.num_experts)
     recv = gather_rows(x, token_of_row)
-    out = expert_ffn(recv, offsets, get_expert)
+    out = expert_ffn(recv, offsets, get_expert, act_quant)
     shared = None
     if spec.num_shared and get_shared is not None:
         ws13, ws2 = get_shared()
-        shared = swiglu_expert(x, ws13, ws2)
+        shared = swiglu_expert(x, ws13, ws2, act_quant)
     return combine(out, row_of, w, shared)
 
 
-def dense_token(x_t, idx_t, w_t, get_expert, get_shared=None):
+def dense_token(x_t, idx_t, w_t, get_expert, get_shared=None, act_quant=False):
     """Brute-force output of one token: loop over its k experts and the shared
-    expert directly from x and the weights, never touching a dispatch buffer."""
+    expert directly from x and the weights, never touching a dispatch buffer.
+    act_quant as in swiglu_expert, applied to this token's row alone."""
     x_t = np.asarray(x_t, dtype=np.float64)
-    y = np.zeros(x_t.shape[0], dtype=np.float64)
-    for j in range(len(idx_t)):
-        w13, w2 = get_expert(int(idx_t[j]))
+    if act_quant:
+        x_t = dequant_rows_1x128(*quantize_rows_1x128(x_t[None, :].astype(np.float32)))[0]
+
+    def one(w13, w2):
         w13 = np.asarray(w13, dtype=np.float64)
         F = w13.shape[0] // 2
         g = np.array([np.dot(w13[i], x_t) for i in range(F)])
         u = np.array([np.dot(w13[F + i], x_t) for i in range(F)])
         h = g / (1.0 + np.exp(-g)) * u
-        y += float(w_t[j]) * (np.asarray(w2, dtype=np.float64) @ h)
+        if act_quant:
+            h = dequant_rows_1x128(*quantize_rows_1x128(h[None, :].astype(np.float32)))[0]
+        return np.asarray(w2, dtype=np.float64) @ h
+
+    y = np.zeros(x_t.shape[0], dtype=np.float64)
+    for j in range(len(idx_t)):
+        y += float(w_t[j]) * one(*get_expert(int(idx_t[j])))
     if get_shared is not None:
-        ws13, ws2 = get_shared()
-        ws13 = np.asarray(ws13, dtype=np.float64)
-        Fs = ws13.shape[0] // 2
-        g = ws13[:Fs] @ x_t
-        u = ws13[Fs:] @ x_t
-        y += np.asarray(ws2, dtype=np.float64) @ (g / (1.0 + np.exp(-g)) * u)
+        y += one(*get_shared())
     return y
 
 
@@ -375,6 +390,11 @@ def quantize_rows_1x128(x32):
     scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
     q = (blocks / scale[:, :, None]).astype(np.float32)
     return e4m3_encode(q).reshape(n, d), scale
+
+
+def dequant_rows_1x128(codes, scales):
+    """Values code * scale of per-row, per-128-column quantised rows."""
+    return e4m3_decode(codes) * np.repeat(np.asarray(scales, dtype=np.float64), 128, axis=1)
 
 
 def dequant_blocks(codes, scales, block=128):

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+that include/moe.h declares, and rejects bad arguments before launching
+anything (none of these calls reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import combine_experts_amd as M
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+@pytest.fixture
+def M():
+    import combine_experts_amd
+    return combine_experts_amd
+
+
+def dsv3(M, **kw):
+    base = dict(num_experts=256, top_k=8, d_model=7168, d_ff=2048, num_shared=1, d_ff_shared=2048, n_group=8,
+                topk_group=4, score="sigmoid", weight="norm_sum", routed_scale=2.5, act_dtype="bf16",
+                weight_dtype="bf16")
+    base.update(kw)
+    return M.make_config(**base)
+
+
+def test_status_strings(M):
+    for s in range(5):
+        assert M.moe_status_string(s).startswith("MOE_")
+    assert "unknown" in M.moe_status_string(99)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_experts=0), 1), (dict(num_experts=2048), 1), (dict(top_k=0), 1), (dict(top_k=300), 1),
+    (dict(n_group=3), 1), (dict(topk_group=9), 1), (dict(topk_group=0), 1),
+    (dict(top_k=8, n_group=8, topk_group=1, num_experts=32), 1),  # k > kg * E / G
+    (dict(num_shared=2), 1), (dict(d_ff_shared=0), 1), (dict(d_model=-128), 1),
+    (dict(routed_scale=float("nan")), 1), (dict(act_dtype="fp8"), 2), (dict(act_dtype="f32"), 2),
+    (dict(d_model=7168 + 64), 2), (dict(weight_dtype="fp8", d_ff=2048 + 128), 2),
+])
+def test_invalid_configs_rejected_before_launch(M, kw, status):
+    cfg = dsv3(M, **kw)
+    assert M.moe_workspace_size(cfg, 16) == 0
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer(cfg, 4, 16, 16, None, M.make_weights(16, 16, 16, 16), 16, 16, 1 << 40, stream=0)
+    assert e.value.status == status
+
+
+def test_zero_tokens_is_a_no_op(M):
+    cfg = dsv3(M)
+    # T = 0 returns before looking at any pointer
+    M.moe_layer(cfg, 0, None, None, None, M.make_weights(None, None), None, None, 0, stream=0)
+    M.moe_route(cfg, 0, None, None, None, None, None, None, stream=0)
+    M.moe_dispatch(cfg, 0, None, None, None, None, None, None, None, None, stream=0)
+    M.moe_combine(cfg, 0, None, None, None, None, None, None, stream=0)
+
+
+def test_negative_tokens_rejected(M):
+    with pytest.raises(M.MoeError):
+        M.moe_route(dsv3(M), -1, 16, None, 16, 16, 16, 16, stream=0)
+
+
+def test_null_and_misaligned_pointers_rejected(M):
+    cfg = dsv3(M)
+    W = M.make_weights(256, 256, 256, 256)
+    with pytest.raises(M.MoeError) as e:
+        M.moe_route(cfg, 4, None, None, 16, 16, 16, 16, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_route(cfg, 4, 18, None, 16, 16, 16, 16, stream=0)  # misaligned logits
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer(cfg, 4, 16, 16, None, M.make_weights(256, None), 16, 16, 1 << 40, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:  # fp8 needs scales
+        M.moe_layer(dsv3(M, weight_dtype="fp8"), 4, 16, 16, None, W, 16, 16, 1 << 40, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_too_small(M):
+    cfg = dsv3(M)
+    need = M.moe_workspace_size(cfg, 8)
+    assert need > 0
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer(cfg, 8, 16, 16, None, M.make_weights(256, 256, 256, 256), 16, 16, need - 1, stream=0)
+    assert e.value.status == M.MOE_ERR_WORKSPACE_TOO_SMALL
+    fneed = M.moe_ffn_workspace_size(cfg, 8)
+    with pytest.raises(M.MoeError) as e:
+        M.moe_expert_ffn(cfg, 8, 16, None, 16, M.make_weights(256, 256, 256, 256), 16, 16, 16, 16, fneed - 1,
+                         stream=0)
+    assert e.value.status == M.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_workspace_sizes_grow_with_tokens(M):
+    cfg = dsv3(M)
+    sizes = [M.moe_workspace_size(cfg, T) for T in (1, 8, 128, 4096)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    assert M.moe_dispatch_rows(cfg, 128) == 1024
+    assert M.moe_dispatch_rows(dsv3(M, weight_dtype="fp8"), 128) == 1024 + 128
+    assert M.moe_dispatch_rows(dsv3(M, weight_dtype="fp8", num_shared=0), 128) == 1024

@@ -69,9 +69,12 @@ def load_library():
     lib.moe_route.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_dispatch.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_expert_ffn.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, vp, vp, sz, vp]
+    lib.moe_ffn_gate_up.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, sz, vp]
+    lib.moe_ffn_down.argtypes = [cp, i32, vp, wp, vp, sz, vp, vp, vp]
     lib.moe_combine.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_layer.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, sz, vp]
-    for f in (lib.moe_route, lib.moe_dispatch, lib.moe_expert_ffn, lib.moe_combine, lib.moe_layer):
+    for f in (lib.moe_route, lib.moe_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up, lib.moe_ffn_down,
+              lib.moe_combine, lib.moe_layer):
         f.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -149,6 +152,17 @@ def moe_expert_ffn(cfg, T, recv, recv_scale, expert_offset, weights: MoeWeights,
     _check(load_library().moe_expert_ffn(ctypes.byref(cfg), T, _ptr(recv), _ptr(recv_scale),
                                          _ptr(expert_offset), ctypes.byref(weights), _ptr(x), _ptr(expert_out),
                                          _ptr(shared_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_ffn_gate_up(cfg, T, recv, recv_scale, expert_offset, weights: MoeWeights, x, ws, ws_bytes, stream=None):
+    _check(load_library().moe_ffn_gate_up(ctypes.byref(cfg), T, _ptr(recv), _ptr(recv_scale),
+                                          _ptr(expert_offset), ctypes.byref(weights), _ptr(x), _ptr(ws),
+                                          ws_bytes, _stream(stream)))
+
+
+def moe_ffn_down(cfg, T, expert_offset, weights: MoeWeights, ws, ws_bytes, expert_out, shared_out, stream=None):
+    _check(load_library().moe_ffn_down(ctypes.byref(cfg), T, _ptr(expert_offset), ctypes.byref(weights),
+                                       _ptr(ws), ws_bytes, _ptr(expert_out), _ptr(shared_out), _stream(stream)))
 
 
 def moe_combine(cfg, T, expert_out, row_of, topk_w, shared_out, y, expert_count, stream=None):

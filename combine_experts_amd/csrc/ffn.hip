@@ -1,239 +1,283 @@
 // Grouped expert GEMMs over the dispatch buffer (read in place) and the shared
-// expert.  "7.13 Serving Mixture-of-Experts", section "Expert Parallelism
-// Mechanics", step 3: one grouped GEMM runs all local experts' matmuls in a
-// single launch; section "Prefill vs. Decode": at decode each expert sees a
-// handful of rows, so the pass is bound by streaming the touched experts'
-// weights.
+// expert, for decode-sized batches.  "7.13 Serving Mixture-of-Experts",
+// section "Expert Parallelism Mechanics", step 3: one grouped GEMM runs all
+// local experts' matmuls in a single launch; section "Prefill vs. Decode": at
+// decode each expert sees a handful of rows, so the pass is bound by streaming
+// the touched experts' weights from HBM.
 //
-// Design (gfx950): the weights are the MFMA A operand and go straight from
-// HBM into registers, 256 bytes of each of 16 rows per step and lane group;
-// the activation rows are the B operand (16 tokens per tile).  A workgroup
-// owns one (group, tile) item; its KS waves split the reduction dimension and
-// are summed through LDS in a fixed order, so results do not depend on timing.
-// Experts with no rows own no items and their weights are never read.
+// Design (gfx950):
+//  * The weights are the MFMA A operand and go straight from HBM into
+//    registers: each step a wave reads 256 bytes of each of its 16 rows.  The
+//    activation rows (one 16-token tile per MFMA column block) are the B
+//    operand.  Experts with no rows own no work, so their weights are never
+//    read.
+//  * Work item = (group, tile of 16*FW output columns).  Groups are the
+//    experts that received rows, in index order, then the shared expert.  A
+//    workgroup has FW x KS waves: FW column tiles, each reduction dimension
+//    split KS ways; the KS partial sums are added through LDS in a fixed order
+//    (results do not depend on timing or slot order).
+//  * Workgroups are persistent: each walks items blockIdx.x, +gridDim.x, ...
+//    and every wave streams its sequence of (item, token chunk, K-step)
+//    stages through a three-slot register ring, two stages ahead, across item
+//    boundaries, so loads stay in flight while an item's epilogue runs.
+//    Loads are never skipped (a stage past the end repeats the last address,
+//    a token row past a group's end reads the group's first row and its
+//    column is never stored), which keeps the wait counts exact.
 #include "moe_kernels.h"
 
 namespace moe {
 
-// Find this block's item: the rank-a non-empty expert, and the number of
-// non-empty experts.  Wave 0 scans expert_offset (E <= 1024, 16 per lane).
-__device__ __forceinline__ void find_group(const int* off, int E, int a, int* out_group, int* out_nactive) {
-  const int lane = threadIdx.x & 63;
-  int cnt = 0;
-  const int e0 = lane * 16;
-  int prev = e0 < E ? off[e0] : 0;
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int e = e0 + i;
-    if (e < E) {
-      const int nxt = off[e + 1];
-      cnt += nxt > prev ? 1 : 0;
-      prev = nxt;
-    }
-  }
-  int inc = cnt;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  const int total = __shfl(inc, 63);
-  const int before = inc - cnt;
-  if (lane == 0) *out_nactive = total;
-  if (a >= before && a < inc) {
-    int seen = before;
-    prev = off[e0];
-    for (int i = 0; i < 16; ++i) {
-      const int e = e0 + i;
-      const int nxt = off[e + 1];
-      if (nxt > prev) {
-        if (seen == a) { *out_group = e; break; }
-        ++seen;
-      }
-      prev = nxt;
-    }
-  }
-}
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int DT, int NMAT, int TT>
-struct Regs {
+// One pipeline stage of a wave: NMAT weight tiles and the activation tiles
+// they multiply (NX = 1: every weight tile walks K in the same order).
+template <int DT, int NMAT, int TT, int NX>
+struct Stage {
   Step w[NMAT];
-  Step x[TT];
-  float sx[TT][2];  // E4M3 activation scales of the step's two 128-blocks
+  Step x[NX][TT];
+  float sx[NX][TT][2]; // E4M3 activation scales of the step's two 128-blocks
+  float sw[NMAT][2];   // E4M3 weight block scales of the step
 };
 
-template <int DT, int FW, int KS, int TT, bool GATED, int OUT>
-__global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
-  constexpr int NMAT = GATED ? 2 : 1;
-  constexpr int ES = Elem<DT>::kBytes;
-  constexpr int STEP = Elem<DT>::kStep;
-  constexpr bool FP8 = DT == MOE_FP8_E4M3;
-  constexpr int RED = (KS > 1 ? (KS - 1) : 1) * FW * NMAT * TT * 4 * 64;
-  __shared__ float red[RED];
-  __shared__ float amax_s[FW][TT * 16];
-  __shared__ int s_group, s_nactive;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
-  const int ft = wid % FW, kp = wid / FW;
-
-  // ---- resolve the item
-  if (wid == 0) {
-    if (lane == 0) s_group = -1;
-    // lane 0's write must land before find_group's writes
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    int a = (int)(blockIdx.x / p.tiles_r);
-    find_group(p.expert_offset, p.E, a, &s_group, &s_nactive);
-  }
-  __syncthreads();
-  const int n_active = s_nactive;
-  int item = blockIdx.x;
-  bool shared;
-  int g, tile;
-  if (item < n_active * p.tiles_r) {
-    shared = false;
-    g = s_group;
-    tile = item % p.tiles_r;
-  } else {
-    item -= n_active * p.tiles_r;
-    if (item >= p.n_shared * p.tiles_s) return;  // uniform per block
-    shared = true;
-    g = 0;
-    tile = item;
-  }
-
-  int rows0, nrows, K, Nout;
-  const uint8_t *act, *wmat;
-  const float *act_scale = nullptr, *w_scale = nullptr;
+// Everything about one item that the loads and the epilogue need; all fields
+// are uniform across the wave.
+struct Item {
+  int valid;
+  int rows0, nrows, nchunks, K, Nout, col0, s_begin, s_end, rot;
+  const uint8_t* w;
+  const uint8_t* act;
+  const float* act_scale;
+  const float* w_scale;
   void* out;
   float* out_scale;
-  size_t wrows;
-  if (!shared) {
-    rows0 = p.expert_offset[g];
-    nrows = p.expert_offset[g + 1] - rows0;
-    K = p.K_r;
-    Nout = p.Nout_r;
-    wrows = (size_t)p.NW_r;
-    act = p.act;
-    wmat = p.w + (size_t)g * wrows * K * ES;
-    if (FP8) {
-      act_scale = p.act_scale;
-      w_scale = p.w_scale + (size_t)g * (wrows / 128) * (K / 128);
+};
+
+struct Cursor {
+  Item it;
+  int item, chunk, step;
+};
+
+template <int DT, int FW, int KS, int TT, int WC>
+struct Walker {
+  static constexpr int ES = Elem<DT>::kBytes;
+  static constexpr int STEP = Elem<DT>::kStep;
+  const FfnParams& p;
+  const int* s_off;
+  const int* s_act;
+  int n_routed_items, n_items, ft, kp;
+
+  __device__ Item decode(int item) const {
+    Item it{};
+    it.valid = item < n_items;
+    if (!it.valid) return it;
+    int tile, K;
+    if (item < n_routed_items) {
+      const int a = item / p.tiles_r;
+      tile = item - a * p.tiles_r;
+      const int g = uni(s_act[a]);
+      it.rows0 = uni(s_off[g]);
+      it.nrows = uni(s_off[g + 1]) - it.rows0;
+      K = p.K_r;
+      it.Nout = p.Nout_r;
+      it.w = p.w + (size_t)g * p.NW_r * K * ES;
+      it.act = p.act;
+      it.act_scale = p.act_scale;
+      it.w_scale = p.w_scale ? p.w_scale + (size_t)g * (p.NW_r / 128) * (K / 128) : nullptr;
+      it.out = p.out;
+      it.out_scale = p.out_scale;
+    } else {
+      tile = item - n_routed_items;
+      it.rows0 = 0;
+      it.nrows = p.T;
+      K = p.K_s;
+      it.Nout = p.Nout_s;
+      it.w = p.s_w;
+      it.act = p.s_act;
+      it.act_scale = p.s_act_scale;
+      it.w_scale = p.s_w_scale;
+      it.out = p.s_out;
+      it.out_scale = p.s_out_scale;
     }
-    out = p.out;
-    out_scale = p.out_scale;
-  } else {
-    rows0 = 0;
-    nrows = p.T;
-    K = p.K_s;
-    Nout = p.Nout_s;
-    wrows = (size_t)p.NW_s;
-    act = p.s_act;
-    wmat = p.s_w;
-    if (FP8) {
-      act_scale = p.s_act_scale;
-      w_scale = p.s_w_scale;
-    }
-    out = p.s_out;
-    out_scale = p.s_out_scale;
+    it.K = K;
+    it.col0 = tile * WC * FW + ft * WC;
+    it.nchunks = (it.nrows + TT * 16 - 1) / (TT * 16);
+    const int steps = K / STEP;
+    it.s_begin = kp * steps / KS;
+    it.s_end = (kp + 1) * steps / KS;
+    // Items start their K walk at different offsets (a fixed function of the
+    // item, so the summation order is reproducible): waves that run in
+    // lockstep then touch different DRAM channels even when rows are a
+    // multiple of the channel interleave apart.
+    it.rot = (int)(((unsigned)item * 2654435761u) >> 16) % (it.s_end - it.s_begin);
+    return it;
   }
 
-  const int col0 = tile * 16 * FW + ft * 16;  // first output column of this wave
-  const size_t rowbytes = (size_t)K * ES;
-  const uint8_t* wrow[NMAT];
-  wrow[0] = wmat + (size_t)(col0 + (lane & 15)) * rowbytes;
-  if (GATED) wrow[NMAT - 1] = wmat + (size_t)(Nout + col0 + (lane & 15)) * rowbytes;
-  const int ksb = K / 128;  // 128-column scale blocks per row
-  int wsrow[NMAT];          // first scale row of each matrix tile (E4M3)
-  wsrow[0] = col0 / 128;
-  if (GATED) wsrow[NMAT - 1] = (Nout + col0) / 128;
+  // K-step actually read at logical position `step` of an item
+  __device__ int phys(const Cursor& c) const {
+    int s = c.step - c.it.s_begin + c.it.rot;
+    const int n = c.it.s_end - c.it.s_begin;
+    if (s >= n) s -= n;
+    return c.it.s_begin + s;
+  }
 
-  const int steps = K / STEP;
-  const int s_begin = kp * steps / KS, s_end = (kp + 1) * steps / KS;
+  __device__ void start(Cursor& c, int item) const {
+    c.item = item;
+    c.it = decode(item);
+    c.chunk = 0;
+    c.step = c.it.s_begin;
+  }
 
-  for (int chunk = 0; chunk < nrows; chunk += TT * 16) {
-    // activation rows of this lane's token column in each tile
-    const uint8_t* xrow[TT];
-    bool xval[TT];
-    int ntile = 0;
-#pragma unroll
-    for (int tt = 0; tt < TT; ++tt) {
-      const int c = chunk + tt * 16 + (lane & 15);
-      xval[tt] = c < nrows;
-      xrow[tt] = act + (size_t)(rows0 + (xval[tt] ? c : 0)) * rowbytes;
-      if (chunk + tt * 16 < nrows) ntile = tt + 1;
+  // Next stage; past the last one the cursor stays put (it.valid stays 1 for
+  // the issue cursor so its loads keep a valid address) and *done is set.
+  __device__ void advance(Cursor& c, bool& done) const {
+    if (++c.step < c.it.s_end) return;
+    if (++c.chunk < c.it.nchunks) {
+      c.step = c.it.s_begin;
+      return;
     }
+    const Item nx = decode(c.item + gridDim.x);
+    if (!nx.valid) {
+      done = true;
+      c.step = c.it.s_end - 1;
+      c.chunk = c.it.nchunks - 1;
+      return;
+    }
+    c.item += gridDim.x;
+    c.it = nx;
+    c.chunk = 0;
+    c.step = c.it.s_begin;
+  }
+};
 
-    f32x4_t acc[NMAT][TT];
+// NM: 16-row weight tiles a wave streams together: the gate and up tiles of
+// the same 16 columns (gated pass), or NM adjacent 16-column tiles (plain).
+template <int DT, int FW, int KS, int TT, bool GATED, int OUT, int NM>
+__global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
+  constexpr int NMAT = GATED ? 2 : NM;
+  constexpr int NX = 1;                     // activation tiles per stage
+  constexpr int WC = GATED ? 16 : 16 * NM;  // output columns per wave
+  constexpr int NT = 64 * FW * KS;
+  constexpr bool FP8 = DT == MOE_FP8_E4M3;
+  constexpr int RED = (KS > 1 ? (KS - 1) : 1) * FW * NMAT * TT * 4 * 64;
+  using W = Walker<DT, FW, KS, TT, WC>;
+  __shared__ float red[RED];
+  __shared__ float amax_s[FW][TT * 16];
+  __shared__ int s_off[1025];
+  __shared__ int s_act[1024];
+  __shared__ int s_wsum[NT / 64];
+
+  const int tid = threadIdx.x;
+  // wave-uniform values go through readfirstlane so that everything derived
+  // from them (item decode, loop bounds) stays in scalar registers and the
+  // loop needs no vector waits beyond the ring's own loads
+  const int lane = tid & 63, wid = uni(tid >> 6);
+  const int ft = wid % FW, kp = wid / FW;
+  const int E = p.E;
+
+  // ---- experts with rows, in index order (once per workgroup)
+  for (int e = tid; e <= E; e += NT) s_off[e] = p.expert_offset[e];
+  __syncthreads();
+  {
+    const int per = (E + NT - 1) / NT;
+    const int e0 = tid * per;
+    int cnt = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E && s_off[e + 1] > s_off[e]) ++cnt;
+    }
+    int inc = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) s_wsum[wid] = inc;
+    __syncthreads();
+    int pos = inc - cnt;
+    for (int w = 0; w < wid; ++w) pos += s_wsum[w];
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E && s_off[e + 1] > s_off[e]) s_act[pos++] = e;
+    }
+  }
+  int n_active = 0;
+  for (int w = 0; w < NT / 64; ++w) n_active += s_wsum[w];
+  n_active = uni(n_active);
+  __syncthreads();
+
+  const W walk{p, s_off, s_act, n_active * p.tiles_r, n_active * p.tiles_r + p.n_shared * p.tiles_s, ft, kp};
+  if ((int)blockIdx.x >= walk.n_items) return;  // uniform per block
+
+  const int r16 = lane & 15;
+  auto load = [&](Stage<DT, NMAT, TT, NX>& s, const Cursor& c) {
+    const size_t rowbytes = (size_t)c.it.K * W::ES;
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      const int ps = walk.phys(c);
+      const int row = (GATED ? (m == 0 ? 0 : c.it.Nout) : 16 * m) + c.it.col0 + r16;
+      load_step(s.w[m], c.it.w + (size_t)row * rowbytes + (size_t)ps * 256, lane);
+      if constexpr (FP8) {
+        const int wsrow = ((GATED ? (m == 0 ? 0 : c.it.Nout) : 16 * m) + c.it.col0) / 128;
+        const float* wsp = c.it.w_scale + (size_t)wsrow * (c.it.K / 128) + 2 * ps;
+        s.sw[m][0] = wsp[0];
+        s.sw[m][1] = wsp[1];
+      }
+    }
+#pragma unroll
+    for (int xi = 0; xi < NX; ++xi) {
+      const int ps = walk.phys(c);
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        int col = c.chunk * TT * 16 + tt * 16 + r16;
+        col = col < c.it.nrows ? col : 0;  // rows past the group's end: never stored
+        const size_t row = (size_t)(c.it.rows0 + col);
+        load_step(s.x[xi][tt], c.it.act + row * rowbytes + (size_t)ps * 256, lane);
+        if constexpr (FP8) {
+          const float* sp = c.it.act_scale + row * (c.it.K / 128) + 2 * ps;
+          s.sx[xi][tt][0] = sp[0];
+          s.sx[xi][tt][1] = sp[1];
+        }
+      }
+    }
+  };
+
+  f32x4_t acc[NMAT][TT];
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) acc[m][tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
 
-    auto load = [&](Regs<DT, NMAT, TT>& r, int s) {
-      const size_t kb = (size_t)s * 256;
+  auto compute = [&](const Stage<DT, NMAT, TT, NX>& s, const Cursor& c) {
+    const int left = c.it.nrows - c.chunk * TT * 16;  // rows of this chunk (> 0)
+    if constexpr (FP8) {
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) load_step(r.w[m], wrow[m] + kb, lane);
+      for (int m = 0; m < NMAT; ++m) {
+        const float sw0 = s.sw[m][0], sw1 = s.sw[m][1];
 #pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        if (tt < ntile) {
-          if (xval[tt]) {
-            load_step(r.x[tt], xrow[tt] + kb, lane);
-            if (FP8) {
-              const float* sp = act_scale + (size_t)(rows0 + chunk + tt * 16 + (lane & 15)) * ksb + 2 * s;
-              r.sx[tt][0] = sp[0];
-              r.sx[tt][1] = sp[1];
-            }
-          } else {
-            zero_step(r.x[tt]);
-            if (FP8) { r.sx[tt][0] = 0.f; r.sx[tt][1] = 0.f; }
+        for (int tt = 0; tt < TT; ++tt) {
+          if (tt * 16 < left) {
+            const int xi = 0;
+            const f32x4_t p0 = mma_fp8_block(s.w[m], s.x[xi][tt], 0);
+            const f32x4_t p1 = mma_fp8_block(s.w[m], s.x[xi][tt], 1);
+            const float c0 = sw0 * s.sx[xi][tt][0], c1 = sw1 * s.sx[xi][tt][1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[m][tt][j] += p0[j] * c0 + p1[j] * c1;
           }
         }
       }
-    };
-    auto compute = [&](const Regs<DT, NMAT, TT>& r, int s) {
-      if constexpr (FP8) {
+    } else {
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-          const float* wsp = w_scale + (size_t)wsrow[m] * ksb + 2 * s;
-          const float sw0 = wsp[0], sw1 = wsp[1];
+      for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-          for (int tt = 0; tt < TT; ++tt) {
-            if (tt < ntile) {
-              const f32x4_t p0 = mma_fp8_block(r.w[m], r.x[tt], 0);
-              const f32x4_t p1 = mma_fp8_block(r.w[m], r.x[tt], 1);
-              const float c0 = sw0 * r.sx[tt][0], c1 = sw1 * r.sx[tt][1];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[m][tt][j] += p0[j] * c0 + p1[j] * c1;
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            if (tt < ntile) Mma<DT>::run(acc[m][tt], r.w[m], r.x[tt]);
-      }
-    };
-
-    // software pipeline: the next step's loads are in flight during this step's MFMAs
-    if (s_begin < s_end) {
-      Regs<DT, NMAT, TT> ra, rb;
-      int s = s_begin;
-      load(ra, s);
-      while (true) {
-        if (s + 1 < s_end) load(rb, s + 1);
-        compute(ra, s);
-        if (++s >= s_end) break;
-        if (s + 1 < s_end) load(ra, s + 1);
-        compute(rb, s);
-        if (++s >= s_end) break;
-      }
+        for (int tt = 0; tt < TT; ++tt)
+          if (tt * 16 < left) Mma<DT>::run(acc[m][tt], s.w[m], s.x[0][tt]);
     }
+  };
 
-    // ---- reduce the KS partial sums (fixed order kp = 1, 2, ...)
+  // End of a (item, chunk): add the KS partial sums, apply the epilogue.
+  auto finish = [&](f32x4_t (&acc)[NMAT][TT], const Cursor& c) {
     if constexpr (KS > 1) {
       if (kp > 0) {
         float* dst = red + ((size_t)((kp - 1) * FW + ft) * NMAT * TT * 4) * 64;
@@ -257,17 +301,15 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
         }
       }
     }
-
-    // ---- epilogue: lane holds output columns col0 + 4 (lane/16) + j of token
-    // column chunk + tt*16 + lane%16
-    const int cfirst = col0 + 4 * (lane >> 4);
+    // lane holds output columns col0 + 4 (lane/16) + j of token chunk*TT*16 + tt*16 + lane%16
+    const int cfirst = c.it.col0 + 4 * (lane >> 4);
+    const int Nout = c.it.Nout;
     if constexpr (GATED) {
       float h[TT][4];
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int j = 0; j < 4; ++j) h[tt][j] = silu(acc[0][tt][j]) * acc[1][tt][j];
-
       if constexpr (OUT == MOE_FP8_E4M3) {
         // per-token amax over the item's 128 columns, then E4M3 codes
         if (kp == 0) {
@@ -283,34 +325,35 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
         if (kp == 0) {
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) {
-            const int c = chunk + tt * 16 + (lane & 15);
-            if (c < nrows) {
+            const int col = c.chunk * TT * 16 + tt * 16 + r16;
+            if (col < c.it.nrows) {
               float a = 0.f;
 #pragma unroll
-              for (int f = 0; f < FW; ++f) a = fmaxf(a, amax_s[f][tt * 16 + (lane & 15)]);
+              for (int f = 0; f < FW; ++f) a = fmaxf(a, amax_s[f][tt * 16 + r16]);
               const float scale = a > 0.f ? a / 448.0f : 1.0f;
               uint32_t word = 0;
 #pragma unroll
               for (int j = 0; j < 4; ++j) word |= f32_to_e4m3(h[tt][j] / scale) << (8 * j);
-              const size_t r = (size_t)(rows0 + c);
-              *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + r * Nout + cfirst) = word;
-              if (ft == 0 && lane < 16) out_scale[r * (Nout / 128) + col0 / 128] = scale;
+              const size_t r = (size_t)(c.it.rows0 + col);
+              *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(c.it.out) + r * Nout + cfirst) = word;
+              if (ft == 0 && lane < 16) c.it.out_scale[r * (Nout / 128) + c.it.col0 / 128] = scale;
             }
           }
         }
       } else if (kp == 0) {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-          const int c = chunk + tt * 16 + (lane & 15);
-          if (c < nrows) {
-            const size_t r = (size_t)(rows0 + c);
+          const int col = c.chunk * TT * 16 + tt * 16 + r16;
+          if (col < c.it.nrows) {
+            const size_t r = (size_t)(c.it.rows0 + col);
             if constexpr (OUT == MOE_F32) {
-              *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + r * Nout + cfirst) =
+              *reinterpret_cast<f32x4_t*>(static_cast<float*>(c.it.out) + r * Nout + cfirst) =
                   f32x4_t{h[tt][0], h[tt][1], h[tt][2], h[tt][3]};
             } else {
               const uint32_t lo = f32_to_bf16_bits(h[tt][0]) | (f32_to_bf16_bits(h[tt][1]) << 16);
               const uint32_t hi = f32_to_bf16_bits(h[tt][2]) | (f32_to_bf16_bits(h[tt][3]) << 16);
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + r * Nout + cfirst) = make_uint2(lo, hi);
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(c.it.out) + r * Nout + cfirst) =
+                  make_uint2(lo, hi);
             }
           }
         }
@@ -318,44 +361,152 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
     } else if (kp == 0) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const int c = chunk + tt * 16 + (lane & 15);
-        if (c < nrows) {
-          const size_t r = (size_t)(rows0 + c);
-          *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + r * Nout + cfirst) = acc[0][tt];
+        const int col = c.chunk * TT * 16 + tt * 16 + r16;
+        if (col < c.it.nrows) {
+          const size_t r = (size_t)(c.it.rows0 + col);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(c.it.out) + r * Nout + cfirst + 16 * m) = acc[m][tt];
         }
       }
     }
-    __syncthreads();  // LDS is reused by the next chunk
+    if constexpr (KS > 1 || OUT == MOE_FP8_E4M3) __syncthreads();  // LDS is reused by the next finish
+  };
+
+  // Main loop, three stages per iteration.  The stages are straight-line
+  // code (loads two stages ahead, MFMAs on the current one); a chunk that
+  // ends inside the group parks its accumulator and is finished at the bottom
+  // of the iteration, so no store or barrier sits between a load and its use.
+  // Past the end the cursors stay on their last stage: the extra loads and
+  // MFMAs are harmless and nothing is parked for them.
+  Cursor ic, cc;
+  walk.start(ic, blockIdx.x);
+  walk.start(cc, blockIdx.x);
+  bool idone = false, cdone = false;
+  Stage<DT, NMAT, TT, NX> ring[3];
+  load(ring[0], ic);
+  walk.advance(ic, idone);
+  load(ring[1], ic);
+  walk.advance(ic, idone);
+  zero_acc();
+  while (!cdone) {
+    bool parked[3];
+    Cursor pc[3];
+    f32x4_t pacc[3][NMAT][TT];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+      const bool live = !cdone;
+      load(ring[(r + 2) % 3], ic);
+      walk.advance(ic, idone);
+      compute(ring[r], cc);
+      parked[r] = live && cc.step == cc.it.s_end - 1;
+      if (parked[r]) {
+        pc[r] = cc;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+          for (int tt = 0; tt < TT; ++tt) pacc[r][m][tt] = acc[m][tt];
+        zero_acc();
+      }
+      if (live) walk.advance(cc, cdone);
+    }
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+      if (parked[r]) finish(pacc[r], pc[r]);
   }
 }
 
-template <int DT, int FW, int KS, bool GATED, int OUT>
-static hipError_t launch_tt(const FfnParams& p, int max_rows, int grid, hipStream_t stream) {
-  const dim3 block(64 * FW * KS);
-  if (max_rows <= 16)
-    hipLaunchKernelGGL((ffn_kernel<DT, FW, KS, 1, GATED, OUT>), dim3(grid), block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((ffn_kernel<DT, FW, KS, 2, GATED, OUT>), dim3(grid), block, 0, stream, p);
+template <int DT, int FW, int KS, int TT, bool GATED, int OUT, int NM = 2>
+static hipError_t launch_one(const FfnParams& p, long long max_items, hipStream_t stream) {
+  auto kern = ffn_kernel<DT, FW, KS, TT, GATED, OUT, NM>;
+  static int per_cu = -1, cus = -1;  // constant per kernel and device model
+  if (per_cu < 0) {
+    int dev = 0, n = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * FW * KS, 0) != hipSuccess) n = 1;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 256;
+    cus = c;
+    per_cu = n > 0 ? n : 1;
+  }
+  const long long cap = (long long)per_cu * cus;
+  const int grid = (int)(max_items < cap ? max_items : cap);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * FW * KS), 0, stream, p);
   return hipGetLastError();
+}
+
+// Launch shape of a pass: FW column tiles x KS reduction splits per
+// workgroup, TT token tiles per chunk.  KS must not exceed the K-steps of any
+// item (every wave needs at least one step per item).  The MOE_FFN_* macros
+// pin a shape for launch-shape sweeps.
+struct Plan {
+  int fw, ks, tt;
+};
+
+static Plan plan_of(const FfnParams& p, int step, bool gated, int wdtype) {
+  int steps = p.K_r / step;
+  if (p.n_shared && p.K_s / step < steps) steps = p.K_s / step;
+  // Long reductions are split over 4 waves (keeps enough waves busy when few
+  // experts have rows); shorter ones keep more steps per wave instead.  One
+  // token tile: a group with more than 16 rows is walked in 16-row chunks.
+  Plan pl{1, 4, 1};
+  if (steps < 32) pl = steps >= 8 ? Plan{2, 2, 1} : Plan{gated ? 4 : 2, 1, 1};
+  if (steps < pl.ks) pl = Plan{gated ? 4 : 2, 1, 1};
+  if (gated && wdtype == MOE_FP8_E4M3) pl = Plan{8, 1, 1};
+#ifdef MOE_FFN_FW
+  if (!(gated && wdtype == MOE_FP8_E4M3)) pl.fw = MOE_FFN_FW;
+#endif
+#ifdef MOE_FFN_KS
+  if (!(gated && wdtype == MOE_FP8_E4M3)) pl.ks = MOE_FFN_KS < steps ? MOE_FFN_KS : steps;
+#endif
+#ifdef MOE_FFN_TT
+  pl.tt = MOE_FFN_TT;
+#endif
+  return pl;
+}
+
+template <int DT, bool GATED, int OUT>
+static hipError_t launch_plan(const FfnParams& p, const Plan& pl, long long items, hipStream_t stream) {
+#define MOE_FFN_CASE(FW, KS, TT)                                                  \
+  if (pl.fw == FW && pl.ks == KS && pl.tt == TT)                                  \
+    return launch_one<DT, FW, KS, TT, GATED, OUT>(p, items, stream);
+  MOE_FFN_CASE(1, 4, 1) MOE_FFN_CASE(1, 4, 2)
+  MOE_FFN_CASE(1, 2, 1) MOE_FFN_CASE(1, 2, 2)
+  MOE_FFN_CASE(1, 1, 1) MOE_FFN_CASE(1, 1, 2)
+  MOE_FFN_CASE(4, 1, 1) MOE_FFN_CASE(4, 1, 2)
+  MOE_FFN_CASE(2, 2, 1) MOE_FFN_CASE(2, 2, 2)
+  MOE_FFN_CASE(2, 1, 1) MOE_FFN_CASE(2, 1, 2)
+#undef MOE_FFN_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, int out_dtype, int max_rows, int max_groups,
                       hipStream_t stream) {
-  const long long grid = (long long)max_groups * p.tiles_r + (long long)p.n_shared * p.tiles_s;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int g = (int)grid;
+  (void)out_dtype;
+  (void)max_rows;
+  const int step = wdtype == MOE_F32 ? 64 : wdtype == MOE_BF16 ? 128 : 256;
+  if (p.K_r / step < 1 || (p.n_shared && p.K_s / step < 1)) return hipErrorInvalidValue;
+  const Plan pl = plan_of(p, step, gated, wdtype);
+  // a work item covers FW waves' columns; a plain-pass wave covers two tiles
+  const int per_item = pl.fw * (gated ? 1 : 2);
+  FfnParams q = p;
+  q.tiles_r = p.tiles_r / per_item;
+  q.tiles_s = p.tiles_s / per_item;
+  if (q.tiles_r * per_item != p.tiles_r || q.tiles_s * per_item != p.tiles_s) return hipErrorInvalidValue;
+  const long long items = (long long)max_groups * q.tiles_r + (long long)q.n_shared * q.tiles_s;
+  if (items <= 0) return hipSuccess;
   if (wdtype == MOE_F32) {
-    if (gated) return launch_tt<MOE_F32, 1, 4, true, MOE_F32>(p, max_rows, g, stream);
-    return launch_tt<MOE_F32, 1, 4, false, MOE_F32>(p, max_rows, g, stream);
+    if (gated) return launch_plan<MOE_F32, true, MOE_F32>(q, pl, items, stream);
+    return launch_plan<MOE_F32, false, MOE_F32>(q, pl, items, stream);
   }
   if (wdtype == MOE_BF16) {
-    if (gated) return launch_tt<MOE_BF16, 1, 4, true, MOE_BF16>(p, max_rows, g, stream);
-    return launch_tt<MOE_BF16, 1, 4, false, MOE_F32>(p, max_rows, g, stream);
+    if (gated) return launch_plan<MOE_BF16, true, MOE_BF16>(q, pl, items, stream);
+    return launch_plan<MOE_BF16, false, MOE_F32>(q, pl, items, stream);
   }
-  if (gated) return launch_tt<MOE_FP8_E4M3, 8, 1, true, MOE_FP8_E4M3>(p, max_rows, g, stream);
-  (void)out_dtype;
-  return launch_tt<MOE_FP8_E4M3, 1, 4, false, MOE_F32>(p, max_rows, g, stream);
+  if (gated) {
+    if (pl.tt == 1) return launch_one<MOE_FP8_E4M3, 8, 1, 1, true, MOE_FP8_E4M3>(q, items, stream);
+    return launch_one<MOE_FP8_E4M3, 8, 1, 2, true, MOE_FP8_E4M3>(q, items, stream);
+  }
+  return launch_plan<MOE_FP8_E4M3, false, MOE_F32>(q, pl, items, stream);
 }
 
 }  // namespace moe

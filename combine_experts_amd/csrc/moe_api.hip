@@ -123,24 +123,15 @@ moe_status dispatch_impl(const moe_config* c, int32_t T, const void* x, const in
   return hip_status(launch_dispatch(p, s));
 }
 
-moe_status ffn_impl(const moe_config* c, int32_t T, const void* recv, const float* recv_scale,
-                    const int32_t* offset, const moe_weights* W, const void* x, float* eout, float* sout,
-                    void* ws, hipStream_t s) {
+FfnParams gate_up_params(const moe_config* c, int32_t T, const void* recv, const float* recv_scale,
+                         const int32_t* offset, const moe_weights* W, const void* x, void* ws) {
   const FfnLayout L = ffn_layout(c, T);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  const int wdt = c->weight_dtype;
-  const int hdt = recv_dtype(c);
-  const int E = c->num_experts, d = c->d_model, F = c->d_ff, Fs = c->d_ff_shared;
-  const int ns = c->num_shared;
-  const int max_groups = (int)(((int64_t)T * c->top_k) < E ? (int64_t)T * c->top_k : E);
-  const int max_rows = T;  // no expert takes a token twice; the shared expert takes all T
   const bool q = fp8(c);
-
-  // pass 1: gate/up + SwiGLU -> h
+  const int d = c->d_model, F = c->d_ff, Fs = c->d_ff_shared, ns = c->num_shared;
   FfnParams a{};
-  a.E = E; a.T = T; a.expert_offset = offset; a.n_shared = ns;
-  const int tc1 = ffn_tile_cols(wdt, true);
-  a.tiles_r = F / tc1; a.tiles_s = ns ? Fs / tc1 : 0;
+  a.E = c->num_experts; a.T = T; a.expert_offset = offset; a.n_shared = ns;
+  a.tiles_r = F / 16; a.tiles_s = ns ? Fs / 16 : 0;
   a.act = static_cast<const uint8_t*>(recv); a.act_scale = recv_scale;
   a.w = static_cast<const uint8_t*>(W->w13); a.w_scale = W->w13_scale;
   a.K_r = d; a.NW_r = 2 * F; a.Nout_r = F;
@@ -156,14 +147,18 @@ moe_status ffn_impl(const moe_config* c, int32_t T, const void* recv, const floa
     a.K_s = d; a.NW_s = 2 * Fs; a.Nout_s = Fs;
     a.s_out = base + L.hs; a.s_out_scale = q ? reinterpret_cast<float*>(base + L.hs_scale) : nullptr;
   }
-  moe_status st = hip_status(launch_ffn(a, wdt, true, hdt, max_rows, max_groups, s));
-  if (st != MOE_OK) return st;
+  return a;
+}
 
-  // pass 2: down projection -> expert_out / shared_out (fp32)
+FfnParams down_params(const moe_config* c, int32_t T, const int32_t* offset, const moe_weights* W,
+                      const void* ws, float* eout, float* sout) {
+  const FfnLayout L = ffn_layout(c, T);
+  const uint8_t* base = static_cast<const uint8_t*>(ws);
+  const bool q = fp8(c);
+  const int d = c->d_model, F = c->d_ff, Fs = c->d_ff_shared, ns = c->num_shared;
   FfnParams b{};
-  b.E = E; b.T = T; b.expert_offset = offset; b.n_shared = ns;
-  const int tc2 = ffn_tile_cols(wdt, false);
-  b.tiles_r = d / tc2; b.tiles_s = ns ? d / tc2 : 0;
+  b.E = c->num_experts; b.T = T; b.expert_offset = offset; b.n_shared = ns;
+  b.tiles_r = d / 16; b.tiles_s = ns ? d / 16 : 0;
   b.act = base + L.h; b.act_scale = q ? reinterpret_cast<const float*>(base + L.h_scale) : nullptr;
   b.w = static_cast<const uint8_t*>(W->w2); b.w_scale = W->w2_scale;
   b.K_r = F; b.NW_r = d; b.Nout_r = d;
@@ -174,7 +169,34 @@ moe_status ffn_impl(const moe_config* c, int32_t T, const void* recv, const floa
     b.K_s = Fs; b.NW_s = d; b.Nout_s = d;
     b.s_out = sout;
   }
-  return hip_status(launch_ffn(b, wdt, false, MOE_F32, max_rows, max_groups, s));
+  return b;
+}
+
+int max_groups_of(const moe_config* c, int32_t T) {
+  const int64_t tk = (int64_t)T * c->top_k;
+  return (int)(tk < c->num_experts ? tk : c->num_experts);
+}
+
+// no expert takes a token twice and the shared expert takes all T, so no
+// group has more than T rows
+moe_status gate_up_impl(const moe_config* c, int32_t T, const void* recv, const float* recv_scale,
+                        const int32_t* offset, const moe_weights* W, const void* x, void* ws, hipStream_t s) {
+  const FfnParams a = gate_up_params(c, T, recv, recv_scale, offset, W, x, ws);
+  return hip_status(launch_ffn(a, c->weight_dtype, true, recv_dtype(c), T, max_groups_of(c, T), s));
+}
+
+moe_status down_impl(const moe_config* c, int32_t T, const int32_t* offset, const moe_weights* W, const void* ws,
+                     float* eout, float* sout, hipStream_t s) {
+  const FfnParams b = down_params(c, T, offset, W, ws, eout, sout);
+  return hip_status(launch_ffn(b, c->weight_dtype, false, MOE_F32, T, max_groups_of(c, T), s));
+}
+
+moe_status ffn_impl(const moe_config* c, int32_t T, const void* recv, const float* recv_scale,
+                    const int32_t* offset, const moe_weights* W, const void* x, float* eout, float* sout,
+                    void* ws, hipStream_t s) {
+  moe_status st = gate_up_impl(c, T, recv, recv_scale, offset, W, x, ws, s);
+  if (st != MOE_OK) return st;
+  return down_impl(c, T, offset, W, ws, eout, sout, s);
 }
 
 moe_status combine_impl(const moe_config* c, int32_t T, const float* eout, const int32_t* row_of,
@@ -258,6 +280,38 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t T, const void* recv, co
     return MOE_ERR_INVALID_ARG;
   if (ws_bytes < ffn_layout(cfg, T).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return ffn_impl(cfg, T, recv, recv_scale, expert_offset, w, x, expert_out, shared_out, ws, (hipStream_t)stream);
+}
+
+moe_status moe_ffn_gate_up(const moe_config* cfg, int32_t T, const void* recv, const float* recv_scale,
+                           const int32_t* expert_offset, const moe_weights* w, const void* x, void* ws,
+                           size_t ws_bytes, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if ((st = check_weights(cfg, w)) != MOE_OK) return st;
+  if (!recv || !expert_offset || !ws) return MOE_ERR_INVALID_ARG;
+  if (fp8(cfg) && !recv_scale) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared && !fp8(cfg) && !x) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(recv, expert_offset, ws) || (recv_scale && !aligned16(recv_scale)) || (x && !aligned16(x)))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_layout(cfg, T).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return gate_up_impl(cfg, T, recv, recv_scale, expert_offset, w, x, ws, (hipStream_t)stream);
+}
+
+moe_status moe_ffn_down(const moe_config* cfg, int32_t T, const int32_t* expert_offset, const moe_weights* w,
+                        const void* ws, size_t ws_bytes, float* expert_out, float* shared_out, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if ((st = check_weights(cfg, w)) != MOE_OK) return st;
+  if (!expert_offset || !ws || !expert_out) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_shared && !shared_out) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(expert_offset, ws, expert_out) || (shared_out && !aligned16(shared_out)))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < ffn_layout(cfg, T).total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return down_impl(cfg, T, expert_offset, w, ws, expert_out, shared_out, (hipStream_t)stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out, const int32_t* row_of,

@@ -76,10 +76,9 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, int out_dtype,
                       int max_groups, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
-// Work-partition constants of the grouped GEMMs, also used by the host to size
-// the grid: a gated E4M3 pass covers 128 output columns per item (so each
-// 1x128 activation block is quantised inside one workgroup); every other pass
-// covers 16.
-inline int ffn_tile_cols(int wdtype, bool gated) { return (gated && wdtype == MOE_FP8_E4M3) ? 128 : 16; }
+// FfnParams::tiles_r / tiles_s count 16-column tiles; launch_ffn groups them
+// into the work items of the launch shape it picks (a gated E4M3 pass always
+// covers 128 columns per item, so each 1x128 block of h is quantised inside one
+// workgroup).
 
 }  // namespace moe

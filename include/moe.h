@@ -200,6 +200,22 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t T, const void* recv,
                           float* shared_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The two halves of moe_expert_ffn, for callers that schedule them apart
+ * (moe_expert_ffn is exactly moe_ffn_gate_up followed by moe_ffn_down on the
+ * same workspace).
+ *   moe_ffn_gate_up: h = silu(Wg a) * (Wu a) for every dispatch row a and,
+ *     with a shared expert, for every token of x; h stays in ws (at least
+ *     moe_ffn_workspace_size(cfg, T) bytes; its layout is private).
+ *   moe_ffn_down: expert_out[r] = W2 h[r], shared_out[t] = Ws2 hs[t], reading
+ *     the h that moe_ffn_gate_up left in ws for the same T and routing.
+ */
+moe_status moe_ffn_gate_up(const moe_config* cfg, int32_t T, const void* recv, const float* recv_scale,
+                           const int32_t* expert_offset, const moe_weights* w, const void* x, void* ws,
+                           size_t ws_bytes, void* stream);
+moe_status moe_ffn_down(const moe_config* cfg, int32_t T, const int32_t* expert_offset, const moe_weights* w,
+                        const void* ws, size_t ws_bytes, float* expert_out, float* shared_out, void* stream);
+
+/*
  * moe_combine: y[t] = sum_j topk_w[t][j] * expert_out[row_of[t][j]]
  * (accumulated in fp32 in slot order j = 0..k-1) + shared_out[t], rounded to
  * act_dtype.  Also resets expert_count[0..E) to zero for the next call.

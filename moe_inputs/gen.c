@@ -13,7 +13,8 @@
  * mix64(mix64(seed) ^ (tensor_id * C_TENSOR)).
  *
  * Normals: Box-Muller (1958) on two 24-bit uniforms taken from one 64-bit
- * output, evaluated in double, cosine branch only.
+ * output, evaluated in single precision (glibc logf / cosf / sqrtf), cosine
+ * branch only; mean and std are applied in double.
  *
  * Storage rounding: fp32 -> bf16 is round-to-nearest-even on the bit pattern.
  * fp8 weight blocks (offline model preparation, not the layer's hot path):
@@ -43,10 +44,10 @@ static inline uint64_t draw(uint64_t state, uint64_t index) {
 }
 
 static inline double normal_from_bits(uint64_t r) {
-  const double inv24 = 1.0 / 16777216.0;
-  double u1 = ((double)(r >> 40) + 0.5) * inv24;
-  double u2 = ((double)((r >> 16) & 0xFFFFFFULL) + 0.5) * inv24;
-  return sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925286766559 * u2);
+  const float inv24 = 1.0f / 16777216.0f;
+  float u1 = ((float)(r >> 40) + 0.5f) * inv24;
+  float u2 = ((float)((r >> 16) & 0xFFFFFFULL) + 0.5f) * inv24;
+  return (double)(sqrtf(-2.0f * logf(u1)) * cosf(6.28318530717958647692f * u2));
 }
 
 static inline uint16_t f32_to_bf16_rne(float f) {

@@ -179,15 +179,32 @@ int max_groups_of(const moe_config* c, int32_t T) {
 
 // no expert takes a token twice and the shared expert takes all T, so no
 // group has more than T rows
+// Prefill-sized batches (on average 32 or more rows per expert) take the
+// LDS-tiled bf16 kernel, which reuses each weight tile across 128 token rows;
+// decode-sized ones take the weight-streaming kernel.
+bool use_tiled(const moe_config* c, int32_t T) {
+  return c->weight_dtype == MOE_BF16 && (int64_t)T * c->top_k >= 32LL * c->num_experts;
+}
+
+// bound on the 128-row token tiles over all routed groups
+long long tiled_token_tiles(const moe_config* c, int32_t T) {
+  const long long tk = (long long)T * c->top_k;
+  return (tk + 127) / 128 + max_groups_of(c, T);
+}
+
 moe_status gate_up_impl(const moe_config* c, int32_t T, const void* recv, const float* recv_scale,
                         const int32_t* offset, const moe_weights* W, const void* x, void* ws, hipStream_t s) {
   const FfnParams a = gate_up_params(c, T, recv, recv_scale, offset, W, x, ws);
+  if (use_tiled(c, T))
+    return hip_status(launch_gemm_tiled(a, true, tiled_token_tiles(c, T), s));
   return hip_status(launch_ffn(a, c->weight_dtype, true, recv_dtype(c), T, max_groups_of(c, T), s));
 }
 
 moe_status down_impl(const moe_config* c, int32_t T, const int32_t* offset, const moe_weights* W, const void* ws,
                      float* eout, float* sout, hipStream_t s) {
   const FfnParams b = down_params(c, T, offset, W, ws, eout, sout);
+  if (use_tiled(c, T))
+    return hip_status(launch_gemm_tiled(b, false, tiled_token_tiles(c, T), s));
   return hip_status(launch_ffn(b, c->weight_dtype, false, MOE_F32, T, max_groups_of(c, T), s));
 }
 

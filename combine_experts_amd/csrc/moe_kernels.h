@@ -75,6 +75,10 @@ hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream);
 hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, int out_dtype, int max_rows,
                       int max_groups, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+// LDS-tiled bf16 grouped GEMM for groups with many rows (prefill);
+// max_token_tiles bounds the 128-row token tiles over the routed groups
+// (sizes the persistent grid).  Needs K % 64 == 0 and Nout % 128 == 0.
+hipError_t launch_gemm_tiled(const FfnParams& p, bool gated, long long max_token_tiles, hipStream_t stream);
 
 // FfnParams::tiles_r / tiles_s count 16-column tiles; launch_ffn groups them
 // into the work items of the launch shape it picks (a gated E4M3 pass always

@@ -11,15 +11,19 @@
 //    activation rows (one 16-token tile per MFMA column block) are the B
 //    operand.  Experts with no rows own no work, so their weights are never
 //    read.
-//  * Work item = (group, tile of 16*FW output columns).  Groups are the
-//    experts that received rows, in index order, then the shared expert.  A
-//    workgroup has FW x KS waves: FW column tiles, each reduction dimension
-//    split KS ways; the KS partial sums are added through LDS in a fixed order
+//  * Work item = (group, 16-row chunk of the group's rows, tile of 16*FW
+//    output columns).  Groups are the experts that received rows, in index
+//    order, then the shared expert.  Every chunk is an item of its own, so a
+//    group with many rows (the shared expert sees all T tokens) is spread
+//    over many workgroups that stream the same weights at about the same
+//    time, instead of one workgroup walking K once per chunk.  A workgroup
+//    has FW x KS waves: FW column tiles, each reduction dimension split KS
+//    ways; the KS partial sums are added through LDS in a fixed order
 //    (results do not depend on timing or slot order).
 //  * Workgroups are persistent: each walks items blockIdx.x, +gridDim.x, ...
-//    and every wave streams its sequence of (item, token chunk, K-step)
-//    stages through a three-slot register ring, two stages ahead, across item
-//    boundaries, so loads stay in flight while an item's epilogue runs.
+//    and every wave streams its sequence of (item, K-step) stages through a
+//    three-slot register ring, two stages ahead, across item boundaries, so
+//    loads stay in flight while an item's epilogue runs.
 //    Loads are never skipped (a stage past the end repeats the last address,
 //    a token row past a group's end reads the group's first row and its
 //    column is never stored), which keeps the wait counts exact.
@@ -43,7 +47,7 @@ struct Stage {
 // are uniform across the wave.
 struct Item {
   int valid;
-  int rows0, nrows, nchunks, K, Nout, col0, s_begin, s_end, rot;
+  int rows0, nrows, K, Nout, col0, s_begin, s_end, rot;
   const uint8_t* w;
   const uint8_t* act;
   const float* act_scale;
@@ -54,7 +58,7 @@ struct Item {
 
 struct Cursor {
   Item it;
-  int item, chunk, step;
+  int item, step;
 };
 
 template <int DT, int FW, int KS, int TT, int WC>
@@ -64,19 +68,29 @@ struct Walker {
   const FfnParams& p;
   const int* s_off;
   const int* s_act;
-  int n_routed_items, n_items, ft, kp;
+  const int* s_pre;  // items before active group a; s_pre[n_active] = routed items
+  int n_active, n_routed_items, n_items, ft, kp;
 
   __device__ Item decode(int item) const {
     Item it{};
     it.valid = item < n_items;
     if (!it.valid) return it;
-    int tile, K;
+    int tile, chunk, K, rows0, nrows, key;
     if (item < n_routed_items) {
-      const int a = item / p.tiles_r;
-      tile = item - a * p.tiles_r;
+      // last active group a with s_pre[a] <= item
+      int lo = 0, hi = n_active - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[mid] <= item) lo = mid; else hi = mid - 1;
+      }
+      const int a = uni(lo);
+      const int local = item - uni(s_pre[a]);
+      chunk = local / p.tiles_r;
+      tile = local - chunk * p.tiles_r;
       const int g = uni(s_act[a]);
-      it.rows0 = uni(s_off[g]);
-      it.nrows = uni(s_off[g + 1]) - it.rows0;
+      key = g * p.tiles_r + tile;
+      rows0 = uni(s_off[g]);
+      nrows = uni(s_off[g + 1]) - rows0;
       K = p.K_r;
       it.Nout = p.Nout_r;
       it.w = p.w + (size_t)g * p.NW_r * K * ES;
@@ -86,9 +100,12 @@ struct Walker {
       it.out = p.out;
       it.out_scale = p.out_scale;
     } else {
-      tile = item - n_routed_items;
-      it.rows0 = 0;
-      it.nrows = p.T;
+      const int local = item - n_routed_items;
+      chunk = local / p.tiles_s;
+      tile = local - chunk * p.tiles_s;
+      key = p.E * p.tiles_r + tile;
+      rows0 = 0;
+      nrows = p.T;
       K = p.K_s;
       it.Nout = p.Nout_s;
       it.w = p.s_w;
@@ -100,15 +117,17 @@ struct Walker {
     }
     it.K = K;
     it.col0 = tile * WC * FW + ft * WC;
-    it.nchunks = (it.nrows + TT * 16 - 1) / (TT * 16);
+    it.rows0 = rows0 + chunk * TT * 16;
+    it.nrows = min(TT * 16, nrows - chunk * TT * 16);
     const int steps = K / STEP;
     it.s_begin = kp * steps / KS;
     it.s_end = (kp + 1) * steps / KS;
-    // Items start their K walk at different offsets (a fixed function of the
-    // item, so the summation order is reproducible): waves that run in
+    // Items start their K walk at different offsets: waves that run in
     // lockstep then touch different DRAM channels even when rows are a
-    // multiple of the channel interleave apart.
-    it.rot = (int)(((unsigned)item * 2654435761u) >> 16) % (it.s_end - it.s_begin);
+    // multiple of the channel interleave apart.  The offset is a function of
+    // (group, column tile) only, so every row of a group is summed in the
+    // same order whichever chunk its dispatch slot falls in.
+    it.rot = (int)(((unsigned)key * 2654435761u) >> 16) % (it.s_end - it.s_begin);
     return it;
   }
 
@@ -123,7 +142,6 @@ struct Walker {
   __device__ void start(Cursor& c, int item) const {
     c.item = item;
     c.it = decode(item);
-    c.chunk = 0;
     c.step = c.it.s_begin;
   }
 
@@ -131,20 +149,14 @@ struct Walker {
   // the issue cursor so its loads keep a valid address) and *done is set.
   __device__ void advance(Cursor& c, bool& done) const {
     if (++c.step < c.it.s_end) return;
-    if (++c.chunk < c.it.nchunks) {
-      c.step = c.it.s_begin;
-      return;
-    }
     const Item nx = decode(c.item + gridDim.x);
     if (!nx.valid) {
       done = true;
       c.step = c.it.s_end - 1;
-      c.chunk = c.it.nchunks - 1;
       return;
     }
     c.item += gridDim.x;
     c.it = nx;
-    c.chunk = 0;
     c.step = c.it.s_begin;
   }
 };
@@ -164,7 +176,9 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
   __shared__ float amax_s[FW][TT * 16];
   __shared__ int s_off[1025];
   __shared__ int s_act[1024];
+  __shared__ int s_pre[1025];
   __shared__ int s_wsum[NT / 64];
+  __shared__ int s_isum[NT / 64];
 
   const int tid = threadIdx.x;
   // wave-uniform values go through readfirstlane so that everything derived
@@ -174,38 +188,54 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
   const int ft = wid % FW, kp = wid / FW;
   const int E = p.E;
 
-  // ---- experts with rows, in index order (once per workgroup)
+  // ---- experts with rows, in index order, and the items before each
+  // (chunks x tiles), once per workgroup
   for (int e = tid; e <= E; e += NT) s_off[e] = p.expert_offset[e];
   __syncthreads();
+  constexpr int CH = TT * 16;  // rows per chunk
   {
     const int per = (E + NT - 1) / NT;
     const int e0 = tid * per;
-    int cnt = 0;
+    int cnt = 0, items = 0;
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
-      if (e < E && s_off[e + 1] > s_off[e]) ++cnt;
+      if (e < E) {
+        const int n = s_off[e + 1] - s_off[e];
+        if (n > 0) { ++cnt; items += (n + CH - 1) / CH * p.tiles_r; }
+      }
     }
-    int inc = cnt;
+    int ic = cnt, ii = items;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
+      const int yc = __shfl_up(ic, o), yi = __shfl_up(ii, o);
+      if (lane >= o) { ic += yc; ii += yi; }
     }
-    if (lane == 63) s_wsum[wid] = inc;
+    if (lane == 63) { s_wsum[wid] = ic; s_isum[wid] = ii; }
     __syncthreads();
-    int pos = inc - cnt;
-    for (int w = 0; w < wid; ++w) pos += s_wsum[w];
+    int pc = ic - cnt, pi = ii - items;
+    for (int w = 0; w < wid; ++w) { pc += s_wsum[w]; pi += s_isum[w]; }
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
-      if (e < E && s_off[e + 1] > s_off[e]) s_act[pos++] = e;
+      if (e < E) {
+        const int n = s_off[e + 1] - s_off[e];
+        if (n > 0) {
+          s_act[pc] = e;
+          s_pre[pc] = pi;
+          ++pc;
+          pi += (n + CH - 1) / CH * p.tiles_r;
+        }
+      }
     }
+    if (tid == NT - 1) s_pre[pc] = pi;  // total routed items after the last group
   }
   int n_active = 0;
   for (int w = 0; w < NT / 64; ++w) n_active += s_wsum[w];
   n_active = uni(n_active);
   __syncthreads();
+  const int routed_items = uni(s_pre[n_active]);
+  const int shared_items = p.n_shared ? (p.T + CH - 1) / CH * p.tiles_s : 0;
 
-  const W walk{p, s_off, s_act, n_active * p.tiles_r, n_active * p.tiles_r + p.n_shared * p.tiles_s, ft, kp};
+  const W walk{p, s_off, s_act, s_pre, n_active, routed_items, routed_items + shared_items, ft, kp};
   if ((int)blockIdx.x >= walk.n_items) return;  // uniform per block
 
   const int r16 = lane & 15;
@@ -228,7 +258,7 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
       const int ps = walk.phys(c);
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        int col = c.chunk * TT * 16 + tt * 16 + r16;
+        int col = tt * 16 + r16;
         col = col < c.it.nrows ? col : 0;  // rows past the group's end: never stored
         const size_t row = (size_t)(c.it.rows0 + col);
         load_step(s.x[xi][tt], c.it.act + row * rowbytes + (size_t)ps * 256, lane);
@@ -250,7 +280,7 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
   };
 
   auto compute = [&](const Stage<DT, NMAT, TT, NX>& s, const Cursor& c) {
-    const int left = c.it.nrows - c.chunk * TT * 16;  // rows of this chunk (> 0)
+    const int left = c.it.nrows;  // rows of this item (> 0)
     if constexpr (FP8) {
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
@@ -276,7 +306,7 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
     }
   };
 
-  // End of a (item, chunk): add the KS partial sums, apply the epilogue.
+  // End of an item: add the KS partial sums, apply the epilogue.
   auto finish = [&](f32x4_t (&acc)[NMAT][TT], const Cursor& c) {
     if constexpr (KS > 1) {
       if (kp > 0) {
@@ -301,7 +331,7 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
         }
       }
     }
-    // lane holds output columns col0 + 4 (lane/16) + j of token chunk*TT*16 + tt*16 + lane%16
+    // lane holds output columns col0 + 4 (lane/16) + j of the item's row tt*16 + lane%16
     const int cfirst = c.it.col0 + 4 * (lane >> 4);
     const int Nout = c.it.Nout;
     if constexpr (GATED) {
@@ -325,7 +355,7 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
         if (kp == 0) {
 #pragma unroll
           for (int tt = 0; tt < TT; ++tt) {
-            const int col = c.chunk * TT * 16 + tt * 16 + r16;
+            const int col = tt * 16 + r16;
             if (col < c.it.nrows) {
               float a = 0.f;
 #pragma unroll
@@ -343,7 +373,7 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
       } else if (kp == 0) {
 #pragma unroll
         for (int tt = 0; tt < TT; ++tt) {
-          const int col = c.chunk * TT * 16 + tt * 16 + r16;
+          const int col = tt * 16 + r16;
           if (col < c.it.nrows) {
             const size_t r = (size_t)(c.it.rows0 + col);
             if constexpr (OUT == MOE_F32) {
@@ -361,7 +391,7 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
     } else if (kp == 0) {
 #pragma unroll
       for (int tt = 0; tt < TT; ++tt) {
-        const int col = c.chunk * TT * 16 + tt * 16 + r16;
+        const int col = tt * 16 + r16;
         if (col < c.it.nrows) {
           const size_t r = (size_t)(c.it.rows0 + col);
 #pragma unroll
@@ -374,9 +404,9 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
   };
 
   // Main loop, three stages per iteration.  The stages are straight-line
-  // code (loads two stages ahead, MFMAs on the current one); a chunk that
-  // ends inside the group parks its accumulator and is finished at the bottom
-  // of the iteration, so no store or barrier sits between a load and its use.
+  // code (loads two stages ahead, MFMAs on the current one); an item that
+  // ends inside the iteration parks its accumulator and is finished at the
+  // bottom of the iteration, so no store or barrier sits between a load and its use.
   // Past the end the cursors stay on their last stage: the extra loads and
   // MFMAs are harmless and nothing is parked for them.
   Cursor ic, cc;
@@ -435,54 +465,48 @@ static hipError_t launch_one(const FfnParams& p, long long max_items, hipStream_
 }
 
 // Launch shape of a pass: FW column tiles x KS reduction splits per
-// workgroup, TT token tiles per chunk.  KS must not exceed the K-steps of any
+// workgroup, 16-row token tiles (one per item).  KS must not exceed the K-steps of any
 // item (every wave needs at least one step per item).  The MOE_FFN_* macros
 // pin a shape for launch-shape sweeps.
 struct Plan {
-  int fw, ks, tt;
+  int fw, ks;
 };
 
 static Plan plan_of(const FfnParams& p, int step, bool gated, int wdtype) {
   int steps = p.K_r / step;
   if (p.n_shared && p.K_s / step < steps) steps = p.K_s / step;
   // Long reductions are split over 4 waves (keeps enough waves busy when few
-  // experts have rows); shorter ones keep more steps per wave instead.  One
-  // token tile: a group with more than 16 rows is walked in 16-row chunks.
-  Plan pl{1, 4, 1};
-  if (steps < 32) pl = steps >= 8 ? Plan{2, 2, 1} : Plan{gated ? 4 : 2, 1, 1};
-  if (steps < pl.ks) pl = Plan{gated ? 4 : 2, 1, 1};
-  if (gated && wdtype == MOE_FP8_E4M3) pl = Plan{8, 1, 1};
+  // experts have rows); shorter ones keep more steps per wave instead.
+  Plan pl{1, 4};
+  if (steps < 32) pl = steps >= 8 ? Plan{2, 2} : Plan{gated ? 4 : 2, 1};
+  if (steps < pl.ks) pl = Plan{gated ? 4 : 2, 1};
+  if (gated && wdtype == MOE_FP8_E4M3) pl = Plan{8, 1};
 #ifdef MOE_FFN_FW
   if (!(gated && wdtype == MOE_FP8_E4M3)) pl.fw = MOE_FFN_FW;
 #endif
 #ifdef MOE_FFN_KS
   if (!(gated && wdtype == MOE_FP8_E4M3)) pl.ks = MOE_FFN_KS < steps ? MOE_FFN_KS : steps;
 #endif
-#ifdef MOE_FFN_TT
-  pl.tt = MOE_FFN_TT;
-#endif
   return pl;
 }
 
 template <int DT, bool GATED, int OUT>
 static hipError_t launch_plan(const FfnParams& p, const Plan& pl, long long items, hipStream_t stream) {
-#define MOE_FFN_CASE(FW, KS, TT)                                                  \
-  if (pl.fw == FW && pl.ks == KS && pl.tt == TT)                                  \
-    return launch_one<DT, FW, KS, TT, GATED, OUT>(p, items, stream);
-  MOE_FFN_CASE(1, 4, 1) MOE_FFN_CASE(1, 4, 2)
-  MOE_FFN_CASE(1, 2, 1) MOE_FFN_CASE(1, 2, 2)
-  MOE_FFN_CASE(1, 1, 1) MOE_FFN_CASE(1, 1, 2)
-  MOE_FFN_CASE(4, 1, 1) MOE_FFN_CASE(4, 1, 2)
-  MOE_FFN_CASE(2, 2, 1) MOE_FFN_CASE(2, 2, 2)
-  MOE_FFN_CASE(2, 1, 1) MOE_FFN_CASE(2, 1, 2)
+#define MOE_FFN_CASE(FW, KS)           \
+  if (pl.fw == FW && pl.ks == KS)      \
+    return launch_one<DT, FW, KS, 1, GATED, OUT>(p, items, stream);
+  MOE_FFN_CASE(1, 4)
+  MOE_FFN_CASE(1, 2)
+  MOE_FFN_CASE(1, 1)
+  MOE_FFN_CASE(4, 1)
+  MOE_FFN_CASE(2, 2)
+  MOE_FFN_CASE(2, 1)
 #undef MOE_FFN_CASE
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, int out_dtype, int max_rows, int max_groups,
+hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long routed_rows, int max_groups,
                       hipStream_t stream) {
-  (void)out_dtype;
-  (void)max_rows;
   const int step = wdtype == MOE_F32 ? 64 : wdtype == MOE_BF16 ? 128 : 256;
   if (p.K_r / step < 1 || (p.n_shared && p.K_s / step < 1)) return hipErrorInvalidValue;
   const Plan pl = plan_of(p, step, gated, wdtype);
@@ -492,7 +516,11 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, int out_dtype,
   q.tiles_r = p.tiles_r / per_item;
   q.tiles_s = p.tiles_s / per_item;
   if (q.tiles_r * per_item != p.tiles_r || q.tiles_s * per_item != p.tiles_s) return hipErrorInvalidValue;
-  const long long items = (long long)max_groups * q.tiles_r + (long long)q.n_shared * q.tiles_s;
+  // 16-row chunks over all groups: full chunks plus at most one partial
+  // chunk per group (bounds the items, which sizes the grid)
+  const long long chunks_r = routed_rows / 16 + max_groups;
+  const long long chunks_s = q.n_shared ? (q.T + 15) / 16 : 0;
+  const long long items = chunks_r * q.tiles_r + chunks_s * q.tiles_s;
   if (items <= 0) return hipSuccess;
   if (wdtype == MOE_F32) {
     if (gated) return launch_plan<MOE_F32, true, MOE_F32>(q, pl, items, stream);
@@ -502,10 +530,7 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, int out_dtype,
     if (gated) return launch_plan<MOE_BF16, true, MOE_BF16>(q, pl, items, stream);
     return launch_plan<MOE_BF16, false, MOE_F32>(q, pl, items, stream);
   }
-  if (gated) {
-    if (pl.tt == 1) return launch_one<MOE_FP8_E4M3, 8, 1, 1, true, MOE_FP8_E4M3>(q, items, stream);
-    return launch_one<MOE_FP8_E4M3, 8, 1, 2, true, MOE_FP8_E4M3>(q, items, stream);
-  }
+  if (gated) return launch_one<MOE_FP8_E4M3, 8, 1, 1, true, MOE_FP8_E4M3>(q, items, stream);
   return launch_plan<MOE_FP8_E4M3, false, MOE_F32>(q, pl, items, stream);
 }
 

@@ -197,7 +197,7 @@ moe_status gate_up_impl(const moe_config* c, int32_t T, const void* recv, const 
   const FfnParams a = gate_up_params(c, T, recv, recv_scale, offset, W, x, ws);
   if (use_tiled(c, T))
     return hip_status(launch_gemm_tiled(a, true, tiled_token_tiles(c, T), s));
-  return hip_status(launch_ffn(a, c->weight_dtype, true, recv_dtype(c), T, max_groups_of(c, T), s));
+  return hip_status(launch_ffn(a, c->weight_dtype, true, (long long)T * c->top_k, max_groups_of(c, T), s));
 }
 
 moe_status down_impl(const moe_config* c, int32_t T, const int32_t* offset, const moe_weights* W, const void* ws,
@@ -205,7 +205,7 @@ moe_status down_impl(const moe_config* c, int32_t T, const int32_t* offset, cons
   const FfnParams b = down_params(c, T, offset, W, ws, eout, sout);
   if (use_tiled(c, T))
     return hip_status(launch_gemm_tiled(b, false, tiled_token_tiles(c, T), s));
-  return hip_status(launch_ffn(b, c->weight_dtype, false, MOE_F32, T, max_groups_of(c, T), s));
+  return hip_status(launch_ffn(b, c->weight_dtype, false, (long long)T * c->top_k, max_groups_of(c, T), s));
 }
 
 moe_status ffn_impl(const moe_config* c, int32_t T, const void* recv, const float* recv_scale,

@@ -70,10 +70,11 @@ struct CombineParams {
 
 hipError_t launch_route(const RouteParams& p, hipStream_t stream);
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream);
-// gated: gate/up + SwiGLU pass; otherwise the down pass.  max_rows bounds the
-// rows of any group (T for the shared expert).
-hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, int out_dtype, int max_rows,
-                      int max_groups, hipStream_t stream);
+// gated: gate/up + SwiGLU pass (output dtype: bf16, or E4M3 with scales for
+// E4M3 weights, or f32); otherwise the down pass (f32 output).  routed_rows
+// is T*k and max_groups bounds the experts with rows (both size the grid).
+hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long routed_rows, int max_groups,
+                      hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // LDS-tiled bf16 grouped GEMM for groups with many rows (prefill);
 // max_token_tiles bounds the 128-row token tiles over the routed groups

@@ -11,11 +11,17 @@
 // chunks XOR-swizzled by row so the MFMA operand reads are free of bank
 // conflicts).  Each wave owns a 64 x 64 block (4 x 4 MFMA tiles) and, in the
 // gated pass, holds matching gate and up columns, so SwiGLU is applied in
-// registers; the MFMA is -> v_mfma_f32_16x16x32_bf16.  (WR = 256 when the feature count
-// allows: one token tile then feeds twice as many weight rows.)  Items are
-// ordered (group, token tile, feature tile), so the workgroups running at the
-// same time share token tiles and the hot experts' weight tiles through the
-// L2 and the Infinity Cache.
+// registers (MFMA: v_mfma_f32_16x16x32_bf16).  WR = 256 when the feature
+// count allows: one token tile then feeds twice as many weight rows.  Items
+// are ordered (group, token tile, feature tile), feature tile fastest, so
+// the workgroups running at the same time share token tiles and the hot
+// experts' weight tiles through the L2 and the Infinity Cache.
+//
+// Measured limit: a CU's L1 keeps a bounded number of L2 requests in flight,
+// so at this tile size (48 KB of operands per K step for 4.2 MFLOP) the
+// kernel is bound by the L2 -> CU path, not by MFMA issue; the prefill layer
+// is in any case bounded below by streaming each touched expert's weights
+// from HBM once.
 #include "moe_kernels.h"
 
 namespace moe {

@@ -13,12 +13,24 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Router: one wavefront per token.  Lane l holds experts l*KPL .. l*KPL+KPL-1.
+// Selection is a radix select on wave ballots (no cross-lane shuffles): the
+// k-th largest selection key is found bit by bit from the top, the experts
+// above it are taken, and ties at it go to the lowest indices.  The chosen k
+// are then put in (key descending, index ascending) order through LDS.
 // ---------------------------------------------------------------------------
 
 // Total order of candidates: larger key first, then lower index.
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
+
+// Monotone map of a non-NaN float onto uint32 (a < b <=> ord(a) < ord(b)).
+__device__ __forceinline__ uint32_t ord(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
 
 template <int KPL>
 __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
@@ -27,11 +39,17 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
   const int wid = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wid;
   const int E = p.E;
-  // per-wave LDS: keys[E], scores[E], group scores[64], group chosen[64]
-  float* kbuf = smem + wid * (2 * E + 128);
+  // per-wave LDS: keys[E], scores[E], group scores[64], group chosen[64],
+  // chosen (key, index) in index order [64 + 64], chosen (index, score) in
+  // output order [64 + 64]
+  float* kbuf = smem + wid * (2 * E + 384);
   float* sbuf = kbuf + E;
   float* gbuf = sbuf + E;
   float* cbuf = gbuf + 64;
+  uint32_t* cu = reinterpret_cast<uint32_t*>(cbuf + 64);
+  int* ce = reinterpret_cast<int*>(cu + 64);
+  int* oe = ce + 64;
+  float* os = reinterpret_cast<float*>(oe + 64);
   if (t >= p.T) return;  // uniform per wave; no block barrier is used below
 
   const float* lg = p.logits + (size_t)t * E;
@@ -53,36 +71,51 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
         if (l == l) lmax = fmaxf(lmax, l);
       }
       if (k != k) k = -INFINITY;
+      if (k == 0.f) k = 0.f;  // -0 and +0 compare equal: one ordered value
       kbuf[e] = k;
       sbuf[e] = s;
     }
     key[i] = k;
   }
 
-  // ---- group stage: lane q < G scores group q; the kg best groups survive
+  // ---- group stage: each group's score is the sum of its two largest keys;
+  // the topk_group best groups survive
   const int G = p.n_group;
   const int gsize = E / G;
   bool elig[KPL];
   if (G > 1) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    if (lane < G) {
-      float b1 = -INFINITY, b2 = -INFINITY;
-      for (int j = 0; j < gsize; ++j) {
-        const float v = kbuf[lane * gsize + j];
+    // LPG lanes (a power of two) scan one group together, then merge their
+    // (largest, second largest) pairs with butterflies inside the group
+    int lpg = 1;
+    while (lpg * 2 * G <= 64) lpg *= 2;
+    const int q = lane / lpg, r = lane % lpg;
+    float b1 = -INFINITY, b2 = -INFINITY;
+    if (q < G) {
+      for (int j = r; j < gsize; j += lpg) {
+        const float v = kbuf[q * gsize + j];
         if (v > b1) { b2 = b1; b1 = v; }
         else if (v > b2) b2 = v;
       }
+    }
+    for (int off = 1; off < lpg; off <<= 1) {
+      const float o1 = __shfl_xor(b1, off), o2 = __shfl_xor(b2, off);
+      const float n1 = fmaxf(b1, o1);
+      b2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+      b1 = n1;
+    }
+    if (q < G && r == 0) {
       float gs = gsize == 1 ? b1 : b1 + b2;
       if (gs != gs) gs = -INFINITY;
-      gbuf[lane] = gs;
+      gbuf[q] = gs;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     if (lane < G) {
       const float mine = gbuf[lane];
       int rank = 0;
-      for (int q = 0; q < G; ++q) rank += better(gbuf[q], q, mine, lane) ? 1 : 0;
+      for (int g = 0; g < G; ++g) rank += better(gbuf[g], g, mine, lane) ? 1 : 0;
       cbuf[lane] = rank < p.topk_group ? 1.f : 0.f;
     }
     __builtin_amdgcn_wave_barrier();
@@ -96,55 +129,89 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
 #pragma unroll
     for (int i = 0; i < KPL; ++i) elig[i] = lane * KPL + i < E;
   }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // ---- top-k: k rounds of a wave-wide arg-max on (key desc, index asc)
+  // ---- top-k: u_t = the k-th largest ordered key among eligible experts,
+  // found bit by bit (count(u >= t) >= k holds for the largest such t)
+  const int k = p.k;
+  uint32_t u[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) u[i] = ord(key[i]);
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) cnt += popc64(__ballot(elig[i] && u[i] >= c));
+    if (cnt >= k) thr = c;
+  }
+  // everything above the threshold is taken; ties at it by lowest index
+  const unsigned long long below = (1ull << lane) - 1ull;  // lanes with lower experts
+  int n_gt = 0, tie_before = 0;
+  bool gt[KPL], eq[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    gt[i] = elig[i] && u[i] > thr;
+    eq[i] = elig[i] && u[i] == thr;
+    n_gt += popc64(__ballot(gt[i]));
+    tie_before += popc64(__ballot(eq[i]) & below);
+  }
+  const int need = k - n_gt;  // >= 1
+  bool sel[KPL];
+  int sel_before = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    sel[i] = gt[i] || (eq[i] && tie_before < need);
+    tie_before += eq[i] ? 1 : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) sel_before += popc64(__ballot(sel[i]) & below);
+  // chosen experts in index order -> LDS
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    if (sel[i]) {
+      cu[sel_before] = u[i];
+      ce[sel_before] = lane * KPL + i;
+      ++sel_before;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  // lane j < k places chosen expert j at its rank in (key desc, index asc)
+  if (lane < k) {
+    const uint32_t uj = cu[lane];
+    const int ej = ce[lane];
+    int pos = 0;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t uo = cu[j];
+      pos += (uo > uj || (uo == uj && ce[j] < ej)) ? 1 : 0;
+    }
+    oe[pos] = ej;
+    os[pos] = sbuf[ej];
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   int my_idx = 0;
   float my_s = 0.f;
-  for (int r = 0; r < p.k; ++r) {
-    float bk = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int e = lane * KPL + i;
-      if (elig[i] && better(key[i], e, bk, bi)) { bk = key[i]; bi = e; }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
-    }
-    // Validation guarantees at least k eligible experts, so a winner always
-    // exists; the clamp only keeps every later index in range regardless.
-    if (bi >= E) bi = 0;
-    // every lane now holds the same winner; its owner retires it
-    if (bi / KPL == lane) {
-#pragma unroll
-      for (int i = 0; i < KPL; ++i)
-        if (lane * KPL + i == bi) elig[i] = false;
-    }
-    if (lane == r) {
-      my_idx = bi;
-      my_s = sbuf[bi];
-    }
+  if (lane < k) {
+    my_idx = oe[lane];
+    my_s = os[lane];
   }
 
   // ---- gate weights from the unbiased scores of the k chosen experts
-  const int k = p.k;
   float w = 0.f;
   if (p.score_fn == MOE_SCORE_SOFTMAX) {
-    // p_e = exp(l_e - M) / Z over all experts
-    float m = lmax;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     if (p.weight_fn == MOE_WEIGHT_NORM_SUM) {
-      // p_j / sum p over the chosen = exp(l_j - M) / sum exp(l_i - M)
+      // p_j / sum p over the chosen = exp(l_j - M) / sum exp(l_i - M); with
+      // M the largest chosen logit (the largest logit overall when G = 1)
+      const float m = os[0];
       float den = 0.f;
-      for (int j = 0; j < k; ++j) den += expf(__shfl(my_s, j) - m);
+      for (int j = 0; j < k; ++j) den += expf(os[j] - m);
       w = expf(my_s - m) / den;
     } else {
+      // p_e = exp(l_e - M) / Z over all experts
+      float m = lmax;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
       float z = 0.f;
 #pragma unroll
       for (int i = 0; i < KPL; ++i) {
@@ -163,13 +230,13 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
   } else {
     if (p.weight_fn == MOE_WEIGHT_NORM_SUM) {
       float den = 0.f;
-      for (int j = 0; j < k; ++j) den += __shfl(my_s, j);
+      for (int j = 0; j < k; ++j) den += os[j];
       w = my_s / den;
     } else {
       float sm = -INFINITY;
-      for (int j = 0; j < k; ++j) sm = fmaxf(sm, __shfl(my_s, j));
+      for (int j = 0; j < k; ++j) sm = fmaxf(sm, os[j]);
       float den = 0.f;
-      for (int j = 0; j < k; ++j) den += expf(__shfl(my_s, j) - sm);
+      for (int j = 0; j < k; ++j) den += expf(os[j] - sm);
       w = expf(my_s - sm) / den;
     }
   }
@@ -186,7 +253,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
 hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
   const int kpl_needed = (p.E + 63) / 64;
   const int blocks = (p.T + 3) / 4;
-  const size_t lds = 4 * (2 * (size_t)p.E + 128) * sizeof(float);
+  const size_t lds = 4 * (2 * (size_t)p.E + 384) * sizeof(float);
 #define MOE_ROUTE_CASE(K)                                                                \
   if (kpl_needed <= K) {                                                                 \
     hipLaunchKernelGGL(route_kernel<K>, dim3(blocks), dim3(256), lds, stream, p);        \

@@ -19,11 +19,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int* rows = p.row_of + (size_t)t * k;
   const float* w = p.topk_w + (size_t)t * k;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.expert_out + (size_t)rows[j] * p.d + c);
-    const float wj = w[j];
+  // eight slots at a time: their row indices and weights first, then all
+  // eight row loads in flight together, then the FMAs in slot order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int r[8];
+    float wj[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
+    for (int j = 0; j < 8; ++j) {
+      r[j] = j0 + j < k ? rows[j0 + j] : 0;
+      wj[j] = j0 + j < k ? w[j0 + j] : 0.f;
+    }
+    f32x4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j0 + j < k) v[j] = *reinterpret_cast<const f32x4_t*>(p.expert_out + (size_t)r[j] * p.d + c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j0 + j < k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj[j], v[j][i], acc[i]);
+      }
   }
   if (p.shared_out) {
     const f32x4_t s = *reinterpret_cast<const f32x4_t*>(p.shared_out + (size_t)t * p.d + c);

@@ -269,9 +269,9 @@ hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
 }
 
 // ---------------------------------------------------------------------------
-// Dispatch: one block per token.  Every block recomputes the exclusive scan of
-// the expert counters in LDS (no separate count pass), then writes its token
-// into the rows it reserved.
+// Dispatch: a row of blocks per token.  Every block recomputes the exclusive
+// scan of the expert counters in LDS (no separate count pass), then writes
+// its part of the token into the rows the token reserved.
 // ---------------------------------------------------------------------------
 
 // Exclusive prefix sum of cnt[0..E) into off[0..E] (LDS), 256 threads, E <= 1024.
@@ -307,45 +307,58 @@ __device__ void block_offsets(const int* cnt, int E, int* off, int* wsum) {
   __syncthreads();
 }
 
+// Grid (T, column blocks).  Plain rows: a block copies 4096 bytes of its
+// token (256 threads x 16 B); E4M3 rows: a block quantises four 128-column
+// blocks (one per wave).  The token's bytes and its slot tickets are loaded
+// before the offsets scan so that their latency overlaps it.
 template <int ACT, bool QUANT>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
   __shared__ int off[1025];
   __shared__ int wsum[4];
   __shared__ int rows[65];
   const int t = blockIdx.x;
-  const int tid = threadIdx.x;
-  block_offsets(p.expert_count, p.E, off, wsum);
-  if (blockIdx.x == 0)
-    for (int e = tid; e <= p.E; e += 256) p.expert_offset[e] = off[e];
-  const int k = p.k;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int k = p.k, d = p.d;
+  int my_e = 0, my_ticket = 0;
   if (tid < k) {
     const size_t o = (size_t)t * k + tid;
-    const int r = off[p.topk_idx[o]] + p.ticket[o];
+    my_e = p.topk_idx[o];
+    my_ticket = p.ticket[o];
+  }
+  constexpr int EB = Elem<ACT>::kBytes;
+  // plain: this thread's 16-byte piece; E4M3: this lane's two values of the
+  // wave's 128-column block
+  const int piece = blockIdx.y * 256 + tid;
+  const int pieces = d * EB / 16;
+  const int nb = d / 128;
+  const int blk = blockIdx.y * 4 + wid;
+  i32x4_t v{};
+  uint32_t pair = 0;
+  if constexpr (!QUANT) {
+    if (piece < pieces)
+      v = reinterpret_cast<const i32x4_t*>(static_cast<const uint8_t*>(p.x) + (size_t)t * d * EB)[piece];
+  } else {
+    if (blk < nb)
+      pair = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.x) + (size_t)t * d)[blk * 64 + lane];
+  }
+  block_offsets(p.expert_count, p.E, off, wsum);
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int e = tid; e <= p.E; e += 256) p.expert_offset[e] = off[e];
+  if (tid < k) {
+    const int r = off[my_e] + my_ticket;
     rows[tid] = r;
-    p.row_of[o] = r;
+    if (blockIdx.y == 0) p.row_of[(size_t)t * k + tid] = r;
   }
   if (tid == 0) rows[k] = QUANT && p.shared_rows ? k * p.T + t : -1;
   __syncthreads();
-  const int d = p.d;
   const int nrows = (QUANT && p.shared_rows) ? k + 1 : k;
 
   if constexpr (!QUANT) {
-    // plain copy, 16-byte pieces
-    constexpr int EB = Elem<ACT>::kBytes;
-    const int pieces = d * EB / 16;
-    const i32x4_t* src = reinterpret_cast<const i32x4_t*>(static_cast<const uint8_t*>(p.x) + (size_t)t * d * EB);
-    for (int c = tid; c < pieces; c += 256) {
-      const i32x4_t v = src[c];
+    if (piece < pieces)
       for (int j = 0; j < nrows; ++j)
-        reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d * EB)[c] = v;
-    }
+        reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d * EB)[piece] = v;
   } else {
-    // E4M3 per 128 columns: one wave per 128-column block, 2 columns per lane
-    const int lane = tid & 63, wid = tid >> 6;
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.x) + (size_t)t * d);
-    const int nb = d / 128;
-    for (int b = wid; b < nb; b += 4) {
-      const uint32_t pair = src[b * 64 + lane];
+    if (blk < nb) {  // uniform per wave
       const float v0 = bf16_bits_to_f32(pair & 0xFFFFu), v1 = bf16_bits_to_f32(pair >> 16);
       float amax = fmaxf(fabsf(v0), fabsf(v1));
 #pragma unroll
@@ -355,20 +368,23 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
       const uint16_t codes = (uint16_t)(c0 | (c1 << 8));
       for (int j = 0; j < nrows; ++j) {
         uint8_t* dst = static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d;
-        reinterpret_cast<uint16_t*>(dst + b * 128)[lane] = codes;
-        if (lane == 0) p.recv_scale[(size_t)rows[j] * nb + b] = scale;
+        reinterpret_cast<uint16_t*>(dst + blk * 128)[lane] = codes;
+        if (lane == 0) p.recv_scale[(size_t)rows[j] * nb + blk] = scale;
       }
     }
   }
 }
 
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream) {
-  dim3 grid(p.T), block(256);
+  const dim3 block(256);
   if (p.quant) {
+    const dim3 grid(p.T, (p.d / 128 + 3) / 4);
     hipLaunchKernelGGL((dispatch_kernel<MOE_BF16, true>), grid, block, 0, stream, p);
   } else if (p.act_dtype == MOE_F32) {
+    const dim3 grid(p.T, (p.d * 4 / 16 + 255) / 256);
     hipLaunchKernelGGL((dispatch_kernel<MOE_F32, false>), grid, block, 0, stream, p);
   } else {
+    const dim3 grid(p.T, (p.d * 2 / 16 + 255) / 256);
     hipLaunchKernelGGL((dispatch_kernel<MOE_BF16, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();

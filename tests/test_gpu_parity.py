@@ -32,6 +32,9 @@ ODD = {
     # 128 with a ragged last tile, several feature tiles, shared expert)
     "tiled_small": WL["dsv3"].with_(name="tiled_small", num_experts=8, top_k=2, d_model=256, d_ff=128,
                                     d_ff_shared=256, n_group=2, topk_group=1),
+    # E4M3 with many rows per expert: the gate/up pass takes 32-row chunks
+    "fp8_rows": WL["dsv3_fp8"].with_(name="fp8_rows", num_experts=16, top_k=4, d_model=768, d_ff=256,
+                                     d_ff_shared=512, n_group=4, topk_group=2),
     # d_model not a multiple of 256: the down pass takes 128-row weight tiles
     "tiled_narrow": WL["dsv3"].with_(name="tiled_narrow", num_experts=8, top_k=2, d_model=384, d_ff=256,
                                      d_ff_shared=384, n_group=2, topk_group=1),
@@ -132,7 +135,8 @@ def _touched(wl, inp):
 SMALL_LAYER = [("tiny", 16), ("tiny", 1), ("tiny", 17), ("tiny", 129), ("qwen3", 1), ("qwen3", 8),
                ("qwen3", 32), ("qwen3", 128), ("qwen3", 3), ("k1_groups", 33), ("softmax_sel", 50),
                ("fp8_small", 1), ("fp8_small", 37), ("f32_shared", 40), ("tiled_small", 300),
-               ("tiled_small", 129), ("tiled_narrow", 257), ("qwen3", 512)]
+               ("tiled_small", 129), ("tiled_narrow", 257), ("qwen3", 512),
+               ("fp8_rows", 200), ("fp8_rows", 67)]
 
 
 @pytest.mark.parametrize("name,T", SMALL_LAYER)

@@ -20,14 +20,14 @@
 //    has FW x KS waves: FW column tiles, each reduction dimension split KS
 //    ways; the KS partial sums are added through LDS in a fixed order
 //    (results do not depend on timing or slot order).
-//  * Workgroups are persistent: each walks items blockIdx.x, +gridDim.x, ...
+//  * Workgroups are persistent: workgroup b of n walks items b, b + n, ...
 //    and every wave streams its sequence of (item, K-step) stages through a
 //    three-slot register ring, two stages ahead, across item boundaries, so
 //    loads stay in flight while an item's epilogue runs.
 //    Loads are never skipped (a stage past the end repeats the last address,
 //    a token row past a group's end reads the group's first row and its
 //    column is never stored), which keeps the wait counts exact.
-#include "moe_kernels.h"
+#include "route_body.h"
 
 namespace moe {
 
@@ -69,7 +69,7 @@ struct Walker {
   const int* s_off;
   const int* s_act;
   const int* s_pre;  // items before active group a; s_pre[n_active] = routed items
-  int n_active, n_routed_items, n_items, ft, kp;
+  int n_active, n_routed_items, n_items, ft, kp, nblk;
 
   __device__ Item decode(int item) const {
     Item it{};
@@ -103,7 +103,7 @@ struct Walker {
       const int local = item - n_routed_items;
       chunk = local / p.tiles_s;
       tile = local - chunk * p.tiles_s;
-      key = p.E * p.tiles_r + tile;
+      key = (1 << 20) + tile;  // independent of E: the same whichever launch runs it
       rows0 = 0;
       nrows = p.T;
       K = p.K_s;
@@ -149,13 +149,13 @@ struct Walker {
   // the issue cursor so its loads keep a valid address) and *done is set.
   __device__ void advance(Cursor& c, bool& done) const {
     if (++c.step < c.it.s_end) return;
-    const Item nx = decode(c.item + gridDim.x);
+    const Item nx = decode(c.item + nblk);
     if (!nx.valid) {
       done = true;
       c.step = c.it.s_end - 1;
       return;
     }
-    c.item += gridDim.x;
+    c.item += nblk;
     c.it = nx;
     c.step = c.it.s_begin;
   }
@@ -164,7 +164,7 @@ struct Walker {
 // NM: 16-row weight tiles a wave streams together: the gate and up tiles of
 // the same 16 columns (gated pass), or NM adjacent 16-column tiles (plain).
 template <int DT, int FW, int KS, int TT, bool GATED, int OUT, int NM>
-__global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
+__device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk) {
   constexpr int NMAT = GATED ? 2 : NM;
   constexpr int NX = 1;                     // activation tiles per stage
   constexpr int WC = GATED ? 16 : 16 * NM;  // output columns per wave
@@ -235,8 +235,8 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
   const int routed_items = uni(s_pre[n_active]);
   const int shared_items = p.n_shared ? (p.T + CH - 1) / CH * p.tiles_s : 0;
 
-  const W walk{p, s_off, s_act, s_pre, n_active, routed_items, routed_items + shared_items, ft, kp};
-  if ((int)blockIdx.x >= walk.n_items) return;  // uniform per block
+  const W walk{p, s_off, s_act, s_pre, n_active, routed_items, routed_items + shared_items, ft, kp, nblk};
+  if (bid >= walk.n_items) return;  // uniform per block
 
   const int r16 = lane & 15;
   auto load = [&](Stage<DT, NMAT, TT, NX>& s, const Cursor& c) {
@@ -410,8 +410,8 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
   // Past the end the cursors stay on their last stage: the extra loads and
   // MFMAs are harmless and nothing is parked for them.
   Cursor ic, cc;
-  walk.start(ic, blockIdx.x);
-  walk.start(cc, blockIdx.x);
+  walk.start(ic, bid);
+  walk.start(cc, bid);
   bool idone = false, cdone = false;
   Stage<DT, NMAT, TT, NX> ring[3];
   load(ring[0], ic);
@@ -444,6 +444,11 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
     for (int r = 0; r < 3; ++r)
       if (parked[r]) finish(pacc[r], pc[r]);
   }
+}
+
+template <int DT, int FW, int KS, int TT, bool GATED, int OUT, int NM>
+__global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
+  ffn_body<DT, FW, KS, TT, GATED, OUT, NM>(p, blockIdx.x, gridDim.x);
 }
 
 template <int DT, int FW, int KS, int TT, bool GATED, int OUT, int NM = 2>
@@ -532,6 +537,71 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
   }
   if (gated) return launch_one<MOE_FP8_E4M3, 8, 1, 1, true, MOE_FP8_E4M3>(q, items, stream);
   return launch_plan<MOE_FP8_E4M3, false, MOE_F32>(q, pl, items, stream);
+}
+
+// ---------------------------------------------------------------------------
+// The router next to the shared expert's gate/up pass, in one launch
+// ("Hot-Expert Skew" section, shared experts; the shared expert needs no
+// routing).  The first nroute workgroups route NW tokens each; the others
+// run the persistent gate/up walk over the shared expert's items only (sp has
+// no routed groups), streaming its weights while HBM would otherwise idle
+// behind the router.  bf16 only: on the E4M3 path the shared expert reads the
+// tokens the dispatch quantises.
+// ---------------------------------------------------------------------------
+
+template <int KPL, int FW, int KS>
+__global__ __launch_bounds__(64 * FW * KS) void route_shared_kernel(RouteParams rp, FfnParams sp, int nroute) {
+  extern __shared__ float smem[];
+  if ((int)blockIdx.x < nroute)
+    route_body<KPL, FW * KS>(rp, blockIdx.x, smem);
+  else
+    ffn_body<MOE_BF16, FW, KS, 1, true, MOE_BF16, 2>(sp, blockIdx.x - nroute, gridDim.x - nroute);
+}
+
+template <int KPL, int FW, int KS>
+static hipError_t launch_rs(const RouteParams& rp, const FfnParams& q, long long items, hipStream_t stream) {
+  auto kern = route_shared_kernel<KPL, FW, KS>;
+  constexpr int NT = 64 * FW * KS;
+  const size_t lds = (size_t)(FW * KS) * route_lds_floats(rp.E) * sizeof(float);
+  int dev = 0, n = 0, c = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, lds) != hipSuccess || n < 1) n = 1;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 256;
+  const long long cap = (long long)n * c;
+  const int nroute = (rp.T + FW * KS - 1) / (FW * KS);
+  const int nshared = (int)(items < cap ? items : cap);
+  hipLaunchKernelGGL(kern, dim3(nroute + nshared), dim3(NT), lds, stream, rp, q, nroute);
+  return hipGetLastError();
+}
+
+bool route_shared_supported(const FfnParams& sp, int wdtype) {
+  if (wdtype != MOE_BF16 || !sp.n_shared) return false;
+  const Plan pl = plan_of(sp, 128, true, wdtype);
+  return (pl.fw == 1 && pl.ks == 4) || (pl.fw == 2 && pl.ks == 2);
+}
+
+hipError_t launch_route_shared(const RouteParams& rp, const FfnParams& sp, int wdtype, hipStream_t stream) {
+  if (!route_shared_supported(sp, wdtype)) return hipErrorInvalidValue;
+  const Plan pl = plan_of(sp, 128, true, wdtype);
+  FfnParams q = sp;
+  q.E = 0;  // no routed groups: the walk covers the shared expert only
+  q.tiles_r = sp.tiles_r / pl.fw;
+  q.tiles_s = sp.tiles_s / pl.fw;
+  if (q.tiles_s * pl.fw != sp.tiles_s) return hipErrorInvalidValue;
+  const long long items = (long long)(q.T + 15) / 16 * q.tiles_s;
+  const int kpl = (rp.E + 63) / 64;
+#define MOE_RS_CASE(K)                                                          \
+  if (kpl <= K) {                                                               \
+    if (pl.fw == 1) return launch_rs<K, 1, 4>(rp, q, items, stream);            \
+    return launch_rs<K, 2, 2>(rp, q, items, stream);                            \
+  }
+  MOE_RS_CASE(1)
+  MOE_RS_CASE(2)
+  MOE_RS_CASE(4)
+  MOE_RS_CASE(8)
+  MOE_RS_CASE(16)
+#undef MOE_RS_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

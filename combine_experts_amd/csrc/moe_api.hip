@@ -102,13 +102,18 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 template <typename... P>
 bool all_aligned(P... ps) { return (aligned16(ps) && ...); }
 
-moe_status route_impl(const moe_config* c, int32_t T, const float* logits, const float* bias, int32_t* idx,
-                      float* w, int32_t* count, int32_t* ticket, hipStream_t s) {
+RouteParams route_params(const moe_config* c, int32_t T, const float* logits, const float* bias, int32_t* idx,
+                         float* w, int32_t* count, int32_t* ticket) {
   RouteParams p{};
   p.T = T; p.E = c->num_experts; p.k = c->top_k; p.n_group = c->n_group; p.topk_group = c->topk_group;
   p.score_fn = c->score_fn; p.weight_fn = c->weight_fn; p.routed_scale = c->routed_scale;
   p.logits = logits; p.bias = bias; p.topk_idx = idx; p.topk_w = w; p.expert_count = count; p.ticket = ticket;
-  return hip_status(launch_route(p, s));
+  return p;
+}
+
+moe_status route_impl(const moe_config* c, int32_t T, const float* logits, const float* bias, int32_t* idx,
+                      float* w, int32_t* count, int32_t* ticket, hipStream_t s) {
+  return hip_status(launch_route(route_params(c, T, logits, bias, idx, w, count, ticket), s));
 }
 
 moe_status dispatch_impl(const moe_config* c, int32_t T, const void* x, const int32_t* idx, const int32_t* count,
@@ -368,6 +373,24 @@ moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const floa
   float* eout = reinterpret_cast<float*>(b + L.eout);
   float* sout = cfg->num_shared ? reinterpret_cast<float*>(b + L.sout) : nullptr;
   void* ffn_ws = b + L.ffn;
+  if (cfg->num_shared && !use_tiled(cfg, T)) {
+    // The shared expert needs no routing: its gate/up pass streams its
+    // weights in the router's launch, and the routed pass follows dispatch.
+    const FfnParams a = gate_up_params(cfg, T, recv, recv_scale, offset, w, x, ffn_ws);
+    if (route_shared_supported(a, cfg->weight_dtype)) {
+      const RouteParams rp = route_params(cfg, T, logits, bias, idx, tw, count, ticket);
+      if ((st = hip_status(launch_route_shared(rp, a, cfg->weight_dtype, s))) != MOE_OK) return st;
+      if ((st = dispatch_impl(cfg, T, x, idx, count, ticket, recv, recv_scale, offset, row_of, s)) != MOE_OK)
+        return st;
+      FfnParams routed = a;
+      routed.n_shared = 0;
+      if ((st = hip_status(launch_ffn(routed, cfg->weight_dtype, true, (long long)T * cfg->top_k,
+                                      max_groups_of(cfg, T), s))) != MOE_OK)
+        return st;
+      if ((st = down_impl(cfg, T, offset, w, ffn_ws, eout, sout, s)) != MOE_OK) return st;
+      return combine_impl(cfg, T, eout, row_of, tw, sout, y, count, s);
+    }
+  }
   if ((st = route_impl(cfg, T, logits, bias, idx, tw, count, ticket, s)) != MOE_OK) return st;
   if ((st = dispatch_impl(cfg, T, x, idx, count, ticket, recv, recv_scale, offset, row_of, s)) != MOE_OK) return st;
   if ((st = ffn_impl(cfg, T, recv, recv_scale, offset, w, x, eout, sout, ffn_ws, s)) != MOE_OK) return st;

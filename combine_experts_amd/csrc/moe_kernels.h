@@ -76,6 +76,11 @@ hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream);
 hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long routed_rows, int max_groups,
                       hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+// Router and the shared expert's gate/up pass in one launch (sp: the full
+// gate/up pass parameters; only its shared expert is run).  Supported for
+// bf16 weights whose gate/up launch shape has four waves per workgroup.
+bool route_shared_supported(const FfnParams& sp, int wdtype);
+hipError_t launch_route_shared(const RouteParams& rp, const FfnParams& sp, int wdtype, hipStream_t stream);
 // LDS-tiled bf16 grouped GEMM for groups with many rows (prefill);
 // max_token_tiles bounds the 128-row token tiles over the routed groups
 // (sizes the persistent grid).  Needs K % 64 == 0 and Nout % 128 == 0.

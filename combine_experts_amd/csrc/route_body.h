@@ -1,0 +1,253 @@
+// Router device code, shared by the router kernel and the launch that runs
+// the router next to the shared expert's gate/up pass.
+#pragma once
+
+#include "moe_kernels.h"
+
+namespace moe {
+
+// LDS floats one routing wave needs: keys[E], scores[E], and 384 words of
+// group and selection scratch.
+__host__ __device__ inline int route_lds_floats(int E) { return 2 * E + 384; }
+
+// ---------------------------------------------------------------------------
+// Router: one wavefront per token.  Lane l holds experts l*KPL .. l*KPL+KPL-1.
+// Selection is a radix select on wave ballots (no cross-lane shuffles): the
+// k-th largest selection key is found bit by bit from the top, the experts
+// above it are taken, and ties at it go to the lowest indices.  The chosen k
+// are then put in (key descending, index ascending) order through LDS.
+// ---------------------------------------------------------------------------
+
+// Total order of candidates: larger key first, then lower index.
+__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Monotone map of a non-NaN float onto uint32 (a < b <=> ord(a) < ord(b)).
+__device__ __forceinline__ uint32_t ord(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
+
+// Routes token bid * NW + w with wave w of an NW-wave block; smem holds
+// route_lds_floats(E) floats per wave.
+template <int KPL, int NW>
+__device__ __forceinline__ void route_body(const RouteParams& p, int bid, float* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int t = bid * NW + wid;
+  const int E = p.E;
+  // per-wave LDS: keys[E], scores[E], group scores[64], group chosen[64],
+  // chosen (key, index) in index order [64 + 64], chosen (index, score) in
+  // output order [64 + 64]
+  float* kbuf = smem + wid * route_lds_floats(E);
+  float* sbuf = kbuf + E;
+  float* gbuf = sbuf + E;
+  float* cbuf = gbuf + 64;
+  uint32_t* cu = reinterpret_cast<uint32_t*>(cbuf + 64);
+  int* ce = reinterpret_cast<int*>(cu + 64);
+  int* oe = ce + 64;
+  float* os = reinterpret_cast<float*>(oe + 64);
+  if (t >= p.T) return;  // uniform per wave; no block barrier is used below
+
+  const float* lg = p.logits + (size_t)t * E;
+  float key[KPL];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane * KPL + i;
+    float k = -INFINITY, s = 0.f;
+    if (e < E) {
+      const float l = lg[e];
+      if (p.score_fn == MOE_SCORE_SIGMOID) {
+        // sigmoid evaluated in double and rounded once to fp32
+        s = (float)(1.0 / (1.0 + exp(-(double)l)));
+        k = p.bias ? s + p.bias[e] : s;
+      } else {
+        s = l;
+        k = l;
+        if (l == l) lmax = fmaxf(lmax, l);
+      }
+      if (k != k) k = -INFINITY;
+      if (k == 0.f) k = 0.f;  // -0 and +0 compare equal: one ordered value
+      kbuf[e] = k;
+      sbuf[e] = s;
+    }
+    key[i] = k;
+  }
+
+  // ---- group stage: each group's score is the sum of its two largest keys;
+  // the topk_group best groups survive
+  const int G = p.n_group;
+  const int gsize = E / G;
+  bool elig[KPL];
+  if (G > 1) {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // LPG lanes (a power of two) scan one group together, then merge their
+    // (largest, second largest) pairs with butterflies inside the group
+    int lpg = 1;
+    while (lpg * 2 * G <= 64) lpg *= 2;
+    const int q = lane / lpg, r = lane % lpg;
+    float b1 = -INFINITY, b2 = -INFINITY;
+    if (q < G) {
+      for (int j = r; j < gsize; j += lpg) {
+        const float v = kbuf[q * gsize + j];
+        if (v > b1) { b2 = b1; b1 = v; }
+        else if (v > b2) b2 = v;
+      }
+    }
+    for (int off = 1; off < lpg; off <<= 1) {
+      const float o1 = __shfl_xor(b1, off), o2 = __shfl_xor(b2, off);
+      const float n1 = fmaxf(b1, o1);
+      b2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+      b1 = n1;
+    }
+    if (q < G && r == 0) {
+      float gs = gsize == 1 ? b1 : b1 + b2;
+      if (gs != gs) gs = -INFINITY;
+      gbuf[q] = gs;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane < G) {
+      const float mine = gbuf[lane];
+      int rank = 0;
+      for (int g = 0; g < G; ++g) rank += better(gbuf[g], g, mine, lane) ? 1 : 0;
+      cbuf[lane] = rank < p.topk_group ? 1.f : 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int e = lane * KPL + i;
+      elig[i] = e < E && cbuf[e / gsize] != 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) elig[i] = lane * KPL + i < E;
+  }
+
+  // ---- top-k: u_t = the k-th largest ordered key among eligible experts,
+  // found bit by bit (count(u >= t) >= k holds for the largest such t)
+  const int k = p.k;
+  uint32_t u[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) u[i] = ord(key[i]);
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = thr | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) cnt += popc64(__ballot(elig[i] && u[i] >= c));
+    if (cnt >= k) thr = c;
+  }
+  // everything above the threshold is taken; ties at it by lowest index
+  const unsigned long long below = (1ull << lane) - 1ull;  // lanes with lower experts
+  int n_gt = 0, tie_before = 0;
+  bool gt[KPL], eq[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    gt[i] = elig[i] && u[i] > thr;
+    eq[i] = elig[i] && u[i] == thr;
+    n_gt += popc64(__ballot(gt[i]));
+    tie_before += popc64(__ballot(eq[i]) & below);
+  }
+  const int need = k - n_gt;  // >= 1
+  bool sel[KPL];
+  int sel_before = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    sel[i] = gt[i] || (eq[i] && tie_before < need);
+    tie_before += eq[i] ? 1 : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) sel_before += popc64(__ballot(sel[i]) & below);
+  // chosen experts in index order -> LDS
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    if (sel[i]) {
+      cu[sel_before] = u[i];
+      ce[sel_before] = lane * KPL + i;
+      ++sel_before;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  // lane j < k places chosen expert j at its rank in (key desc, index asc)
+  if (lane < k) {
+    const uint32_t uj = cu[lane];
+    const int ej = ce[lane];
+    int pos = 0;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t uo = cu[j];
+      pos += (uo > uj || (uo == uj && ce[j] < ej)) ? 1 : 0;
+    }
+    oe[pos] = ej;
+    os[pos] = sbuf[ej];
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  int my_idx = 0;
+  float my_s = 0.f;
+  if (lane < k) {
+    my_idx = oe[lane];
+    my_s = os[lane];
+  }
+
+  // ---- gate weights from the unbiased scores of the k chosen experts
+  float w = 0.f;
+  if (p.score_fn == MOE_SCORE_SOFTMAX) {
+    if (p.weight_fn == MOE_WEIGHT_NORM_SUM) {
+      // p_j / sum p over the chosen = exp(l_j - M) / sum exp(l_i - M); with
+      // M the largest chosen logit (the largest logit overall when G = 1)
+      const float m = os[0];
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += expf(os[j] - m);
+      w = expf(my_s - m) / den;
+    } else {
+      // p_e = exp(l_e - M) / Z over all experts
+      float m = lmax;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        const int e = lane * KPL + i;
+        if (e < E) z += expf(sbuf[e] - m);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+      const float pj = expf(my_s - m) / z;
+      float pm = -INFINITY;
+      for (int j = 0; j < k; ++j) pm = fmaxf(pm, __shfl(pj, j));
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += expf(__shfl(pj, j) - pm);
+      w = expf(pj - pm) / den;
+    }
+  } else {
+    if (p.weight_fn == MOE_WEIGHT_NORM_SUM) {
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += os[j];
+      w = my_s / den;
+    } else {
+      float sm = -INFINITY;
+      for (int j = 0; j < k; ++j) sm = fmaxf(sm, os[j]);
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += expf(os[j] - sm);
+      w = expf(my_s - sm) / den;
+    }
+  }
+  w *= p.routed_scale;
+
+  if (lane < k) {
+    const size_t o = (size_t)t * k + lane;
+    p.topk_idx[o] = my_idx;
+    p.topk_w[o] = w;
+    p.ticket[o] = atomicAdd(p.expert_count + my_idx, 1);
+  }
+}
+
+}  // namespace moe

@@ -35,6 +35,10 @@ ODD = {
     # E4M3 with many rows per expert: the gate/up pass takes 32-row chunks
     "fp8_rows": WL["dsv3_fp8"].with_(name="fp8_rows", num_experts=16, top_k=4, d_model=768, d_ff=256,
                                      d_ff_shared=512, n_group=4, topk_group=2),
+    # bf16 with a shared expert and d_model >= 1024: moe_layer runs the shared
+    # expert's gate/up pass inside the router's launch
+    "cosched": WL["dsv3"].with_(name="cosched", num_experts=16, top_k=4, d_model=1024, d_ff=256,
+                                d_ff_shared=512, n_group=4, topk_group=2),
     # d_model not a multiple of 256: the down pass takes 128-row weight tiles
     "tiled_narrow": WL["dsv3"].with_(name="tiled_narrow", num_experts=8, top_k=2, d_model=384, d_ff=256,
                                      d_ff_shared=384, n_group=2, topk_group=1),
@@ -136,7 +140,7 @@ SMALL_LAYER = [("tiny", 16), ("tiny", 1), ("tiny", 17), ("tiny", 129), ("qwen3",
                ("qwen3", 32), ("qwen3", 128), ("qwen3", 3), ("k1_groups", 33), ("softmax_sel", 50),
                ("fp8_small", 1), ("fp8_small", 37), ("f32_shared", 40), ("tiled_small", 300),
                ("tiled_small", 129), ("tiled_narrow", 257), ("qwen3", 512),
-               ("fp8_rows", 200), ("fp8_rows", 67)]
+               ("fp8_rows", 200), ("fp8_rows", 67), ("cosched", 1), ("cosched", 45)]
 
 
 @pytest.mark.parametrize("name,T", SMALL_LAYER)
@@ -177,7 +181,7 @@ def _layer_via_moe_layer(wl, inp, W, ws=None):
 
 
 @pytest.mark.parametrize("name,Ts", [("tiny", (129, 16, 1)), ("qwen3", (128, 8, 1)), ("fp8_small", (37, 5)),
-                                     ("k1_groups", (33, 2))])
+                                     ("k1_groups", (33, 2)), ("cosched", (45, 7, 1))])
 def test_moe_layer_equals_chain_and_reuses_workspace(name, Ts):
     """moe_layer is bit-identical to the four entry points run in turn (the
     results do not depend on slot order or timing), and one zero-filled

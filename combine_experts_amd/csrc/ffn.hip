@@ -70,6 +70,7 @@ struct Walker {
   const int* s_act;
   const int* s_pre;  // items before active group a; s_pre[n_active] = routed items
   int n_active, n_routed_items, n_items, ft, kp, nblk;
+  bool single;  // every active group is one chunk: group a owns items [a tiles_r, (a+1) tiles_r)
 
   __device__ Item decode(int item) const {
     Item it{};
@@ -78,13 +79,20 @@ struct Walker {
     int tile, chunk, K, rows0, nrows, key;
     if (item < n_routed_items) {
       // last active group a with s_pre[a] <= item
-      int lo = 0, hi = n_active - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pre[mid] <= item) lo = mid; else hi = mid - 1;
+      int lo, local;
+      if (single) {
+        lo = item / p.tiles_r;
+        local = item - lo * p.tiles_r;
+      } else {
+        lo = 0;
+        int hi = n_active - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_pre[mid] <= item) lo = mid; else hi = mid - 1;
+        }
+        local = item - uni(s_pre[lo]);
       }
       const int a = uni(lo);
-      const int local = item - uni(s_pre[a]);
       chunk = local / p.tiles_r;
       tile = local - chunk * p.tiles_r;
       const int g = uni(s_act[a]);
@@ -235,7 +243,8 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk) 
   const int routed_items = uni(s_pre[n_active]);
   const int shared_items = p.n_shared ? (p.T + CH - 1) / CH * p.tiles_s : 0;
 
-  const W walk{p, s_off, s_act, s_pre, n_active, routed_items, routed_items + shared_items, ft, kp, nblk};
+  const W walk{p, s_off, s_act, s_pre, n_active, routed_items, routed_items + shared_items, ft, kp, nblk,
+               routed_items == n_active * p.tiles_r};
   if (bid >= walk.n_items) return;  // uniform per block
 
   const int r16 = lane & 15;

@@ -379,6 +379,9 @@ def main():
                 "mfma_frac": round(flops / med / 1e6 / peak_t, 5),
                 "hbm_roof_us": round(nbytes / HBM_PEAK_GBS / 1e3, 2),
                 "mfma_roof_us": round(flops / peak_t / 1e6, 2),
+                # the binding roof is the larger of the two; frac = roof / measured
+                "binding_roof": "hbm" if nbytes / HBM_PEAK_GBS / 1e3 >= flops / peak_t / 1e6 else "mfma",
+                "binding_frac": round(max(nbytes / HBM_PEAK_GBS / 1e3, flops / peak_t / 1e6) / med, 4),
                 "phase_us_mean": {p: round(float(v), 2) for p, v in
                                   zip(("route", "dispatch", "gate_up", "down", "combine"), ph.mean(axis=0))},
                 "gate_up_GBps": round(gu_bytes / gu_us / 1e3, 1),

@@ -99,14 +99,16 @@ def gate_up_work(wl, T, touched):
 class Layer:
     """Weights of one workload in HBM (every expert), generated in chunks."""
 
-    def __init__(self, wl, seed=0):
+    def __init__(self, wl, seed=0, masked=False):
         import torch
         import moe_inputs as mi
         import combine_experts_amd as M
         self.wl = wl
         E, d, F, Fs = wl.num_experts, wl.d_model, wl.d_ff, wl.d_ff_shared
         self.cfg = M.make_config(wl.num_experts, wl.top_k, d, F, wl.num_shared, Fs, wl.n_group, wl.topk_group,
-                                 wl.score, wl.weight, wl.routed_scale, wl.act_dtype, wl.weight_dtype)
+                                 wl.score, wl.weight, wl.routed_scale, wl.act_dtype, wl.weight_dtype,
+                                 masked=masked)
+        self.masked = masked
         fp8 = wl.weight_dtype == "fp8"
         tdt = {"f32": torch.float32, "bf16": torch.int16, "fp8": torch.uint8}[wl.weight_dtype]
         t0 = time.time()
@@ -184,7 +186,8 @@ class Batch:
         self.recv_scale = torch.empty((rows, d // 128), device="cuda") if wl.weight_dtype == "fp8" else None
         self.offset = torch.empty(E + 1, dtype=torch.int32, device="cuda")
         self.row_of = torch.empty((T, k), dtype=torch.int32, device="cuda")
-        self.eout = torch.empty((T * k, d), device="cuda")
+        routed = E * T if layer.masked else T * k
+        self.eout = torch.empty((routed, d), device="cuda")
         self.sout = torch.empty((T, d), device="cuda") if wl.num_shared else None
         self.fws_bytes = M.moe_ffn_workspace_size(cfg, T)
         self.fws = torch.empty(max(self.fws_bytes, 256), dtype=torch.uint8, device="cuda")
@@ -201,13 +204,21 @@ def run_phases(layer, b, marks):
     import combine_experts_amd as M
     cfg, T = layer.cfg, b.T
     marks[0].record()
-    M.moe_route(cfg, T, b.logits, b.bias, b.idx, b.tw, b.count, b.ticket)
-    marks[1].record()
-    M.moe_dispatch(cfg, T, b.x, b.idx, b.count, b.ticket, b.recv, b.recv_scale, b.offset, b.row_of)
+    if layer.masked:
+        # one launch routes and writes the tokens; the GEMMs take the counters
+        M.moe_route_dispatch(cfg, T, b.logits, b.bias, b.x, b.idx, b.tw, b.count, b.ticket, b.recv,
+                             b.recv_scale, b.row_of)
+        marks[1].record()
+        groups = b.count
+    else:
+        M.moe_route(cfg, T, b.logits, b.bias, b.idx, b.tw, b.count, b.ticket)
+        marks[1].record()
+        M.moe_dispatch(cfg, T, b.x, b.idx, b.count, b.ticket, b.recv, b.recv_scale, b.offset, b.row_of)
+        groups = b.offset
     marks[2].record()
-    M.moe_ffn_gate_up(cfg, T, b.recv, b.recv_scale, b.offset, layer.W, b.x, b.fws, b.fws_bytes)
+    M.moe_ffn_gate_up(cfg, T, b.recv, b.recv_scale, groups, layer.W, b.x, b.fws, b.fws_bytes)
     marks[3].record()
-    M.moe_ffn_down(cfg, T, b.offset, layer.W, b.fws, b.fws_bytes, b.eout, b.sout)
+    M.moe_ffn_down(cfg, T, groups, layer.W, b.fws, b.fws_bytes, b.eout, b.sout)
     marks[4].record()
     M.moe_combine(cfg, T, b.eout, b.row_of, b.tw, b.sout, b.y, b.count)
     marks[5].record()
@@ -311,6 +322,9 @@ def main():
     ap.add_argument("--tokens", default=None, help="override the token counts, e.g. 1,8,128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--layout", choices=("compact", "masked"), default="compact",
+                    help="dispatch layout: compact (T*k rows from a scan of the counters) or masked "
+                         "(E*T rows, route and dispatch in one launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (a plain copy of known size for "
                          "scaling the profiler's byte counters) and exit")
@@ -352,7 +366,7 @@ def main():
                 if k_ != key:
                     del layers[k_]
             torch.cuda.empty_cache()
-            layers[key] = Layer(wl)
+            layers[key] = Layer(wl, masked=args.layout == "masked")
         layer = layers[key]  # the prefill workload reuses the decode weights; only the bias differs
         toks = DEFAULT_SWEEP.get(name, wl.tokens)
         if args.tokens:
@@ -368,7 +382,7 @@ def main():
             gu_us = float(ph[:, 2].mean())
             peak_t = MFMA_PEAK_TFLOPS[b_wl.weight_dtype]
             ent = {
-                "workload": WORKLOAD_NAMES[name], "tokens": T, "touched_experts": D,
+                "workload": WORKLOAD_NAMES[name], "tokens": T, "layout": args.layout, "touched_experts": D,
                 "layer_us_median": round(med, 2), "layer_us_p10": round(float(np.percentile(layer_us, 10)), 2),
                 "layer_us_p90": round(float(np.percentile(layer_us, 90)), 2),
                 "tokens_per_s": round(T / med * 1e6, 1),
@@ -417,7 +431,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shapes; random weights)",
-        "config": {"workload": ent["workload"], "tokens": ent["tokens"], "cache": "cold (1 GiB read before each step)"},
+        "config": {"workload": ent["workload"], "tokens": ent["tokens"], "layout": ent["layout"],
+                   "cache": "cold (1 GiB read before each step)"},
     }
     if gu_us:
         out["roofline"] = {"kernel": "ffn_kernel gate/up+SwiGLU (moe_ffn_gate_up)", "bound": "hbm",

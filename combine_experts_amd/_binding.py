@@ -27,7 +27,7 @@ class MoeConfig(ctypes.Structure):
         ("num_experts", _c_i32), ("top_k", _c_i32), ("d_model", _c_i32), ("d_ff", _c_i32),
         ("num_shared", _c_i32), ("d_ff_shared", _c_i32), ("n_group", _c_i32), ("topk_group", _c_i32),
         ("score_fn", _c_i32), ("weight_fn", _c_i32), ("routed_scale", ctypes.c_float),
-        ("act_dtype", _c_i32), ("weight_dtype", _c_i32),
+        ("act_dtype", _c_i32), ("weight_dtype", _c_i32), ("masked_layout", _c_i32),
     ]
 
 
@@ -54,7 +54,7 @@ def load_library():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run combine_experts_amd.build.build() "
+            f"{LIB_PATH} is not built; run `python combine_experts_amd/build.py` "
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     cp = ctypes.POINTER(MoeConfig)
@@ -68,12 +68,13 @@ def load_library():
     lib.moe_workspace_size.restype = sz
     lib.moe_route.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_dispatch.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_route_dispatch.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_expert_ffn.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, vp, vp, sz, vp]
     lib.moe_ffn_gate_up.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, sz, vp]
     lib.moe_ffn_down.argtypes = [cp, i32, vp, wp, vp, sz, vp, vp, vp]
     lib.moe_combine.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_layer.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, sz, vp]
-    for f in (lib.moe_route, lib.moe_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up, lib.moe_ffn_down,
+    for f in (lib.moe_route, lib.moe_dispatch, lib.moe_route_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up, lib.moe_ffn_down,
               lib.moe_combine, lib.moe_layer):
         f.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -84,12 +85,12 @@ def load_library():
 
 def make_config(num_experts, top_k, d_model, d_ff, num_shared=0, d_ff_shared=0, n_group=1, topk_group=1,
                 score="sigmoid", weight="norm_sum", routed_scale=1.0, act_dtype="bf16",
-                weight_dtype="bf16") -> MoeConfig:
+                weight_dtype="bf16", masked=False) -> MoeConfig:
     """Build a moe_config from names ('sigmoid'/'softmax', 'norm_sum'/'softmax_selected',
-    'f32'/'bf16'/'fp8')."""
+    'f32'/'bf16'/'fp8'); masked selects the masked dispatch layout."""
     return MoeConfig(num_experts, top_k, d_model, d_ff, num_shared, d_ff_shared, n_group, topk_group,
                      SCORE[score], WEIGHT[weight], float(routed_scale), DTYPE[act_dtype],
-                     DTYPE[weight_dtype])
+                     DTYPE[weight_dtype], 1 if masked else 0)
 
 
 def make_weights(w13, w2, ws13=None, ws2=None, w13_scale=None, w2_scale=None, ws13_scale=None,
@@ -145,6 +146,13 @@ def moe_dispatch(cfg, T, x, topk_idx, expert_count, ticket, recv, recv_scale, ex
     _check(load_library().moe_dispatch(ctypes.byref(cfg), T, _ptr(x), _ptr(topk_idx), _ptr(expert_count),
                                        _ptr(ticket), _ptr(recv), _ptr(recv_scale), _ptr(expert_offset),
                                        _ptr(row_of), _stream(stream)))
+
+
+def moe_route_dispatch(cfg, T, logits, bias, x, topk_idx, topk_w, expert_count, ticket, recv, recv_scale,
+                       row_of, stream=None):
+    _check(load_library().moe_route_dispatch(ctypes.byref(cfg), T, _ptr(logits), _ptr(bias), _ptr(x),
+                                             _ptr(topk_idx), _ptr(topk_w), _ptr(expert_count), _ptr(ticket),
+                                             _ptr(recv), _ptr(recv_scale), _ptr(row_of), _stream(stream)))
 
 
 def moe_expert_ffn(cfg, T, recv, recv_scale, expert_offset, weights: MoeWeights, x, expert_out, shared_out,

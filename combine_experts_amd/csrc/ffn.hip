@@ -97,8 +97,8 @@ struct Walker {
       tile = local - chunk * p.tiles_r;
       const int g = uni(s_act[a]);
       key = g * p.tiles_r + tile;
-      rows0 = uni(s_off[g]);
-      nrows = uni(s_off[g + 1]) - rows0;
+      rows0 = p.masked ? g * p.T : uni(s_off[g]);
+      nrows = p.masked ? uni(s_off[g]) : uni(s_off[g + 1]) - rows0;
       K = p.K_r;
       it.Nout = p.Nout_r;
       it.w = p.w + (size_t)g * p.NW_r * K * ES;
@@ -198,7 +198,9 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk) 
 
   // ---- experts with rows, in index order, and the items before each
   // (chunks x tiles), once per workgroup
-  for (int e = tid; e <= E; e += NT) s_off[e] = p.expert_offset[e];
+  // compact layout: offsets [E+1]; masked layout: counts [E] (rows of
+  // expert e start at e*T)
+  for (int e = tid; e <= E; e += NT) s_off[e] = p.masked ? (e < E ? p.expert_offset[e] : 0) : p.expert_offset[e];
   __syncthreads();
   constexpr int CH = TT * 16;  // rows per chunk
   {
@@ -208,7 +210,7 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk) 
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
       if (e < E) {
-        const int n = s_off[e + 1] - s_off[e];
+        const int n = p.masked ? s_off[e] : s_off[e + 1] - s_off[e];
         if (n > 0) { ++cnt; items += (n + CH - 1) / CH * p.tiles_r; }
       }
     }
@@ -225,7 +227,7 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk) 
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
       if (e < E) {
-        const int n = s_off[e + 1] - s_off[e];
+        const int n = p.masked ? s_off[e] : s_off[e + 1] - s_off[e];
         if (n > 0) {
           s_act[pc] = e;
           s_pre[pc] = pi;
@@ -605,19 +607,21 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
 // ---------------------------------------------------------------------------
 // The router next to the shared expert's gate/up pass, in one launch
 // ("Hot-Expert Skew" section, shared experts; the shared expert needs no
-// routing).  The first nroute workgroups route NW tokens each; the others
-// run the persistent gate/up walk over the shared expert's items only (sp has
-// no routed groups), streaming its weights while HBM would otherwise idle
-// behind the router.  bf16 only: on the E4M3 path the shared expert reads the
+// routing).  The first nroute workgroups route four tokens each (one, and
+// write it, in the masked layout); the others run the persistent gate/up
+// walk over the shared expert's items only (sp has no routed groups),
+// streaming its weights while HBM would otherwise idle behind the router.  bf16 only: on the E4M3 path the shared expert reads the
 // tokens the dispatch quantises.
 // ---------------------------------------------------------------------------
 
 template <int KPL, int FW, int KS>
 __global__ __launch_bounds__(64 * FW * KS) void route_shared_kernel(RouteParams rp, FfnParams sp, int nroute) {
   extern __shared__ float smem[];
-  if ((int)blockIdx.x < nroute)
-    route_body<KPL, FW * KS>(rp, blockIdx.x, smem);
-  else
+  static_assert(FW * KS == 4, "the routing workgroups hold four waves");
+  if ((int)blockIdx.x < nroute) {
+    if (rp.fuse) route_dispatch_block<KPL>(rp, blockIdx.x, smem);  // one token, masked-layout write
+    else route_body<KPL, 4>(rp, blockIdx.x, smem);                 // four tokens
+  } else
     ffn_body<MOE_BF16, FW, KS, 1, true, MOE_BF16, 2>(sp, blockIdx.x - nroute, gridDim.x - nroute);
 }
 
@@ -631,7 +635,7 @@ static hipError_t launch_rs(const RouteParams& rp, const FfnParams& q, long long
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, lds) != hipSuccess || n < 1) n = 1;
   if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 256;
   const long long cap = (long long)n * c;
-  const int nroute = (rp.T + FW * KS - 1) / (FW * KS);
+  const int nroute = rp.fuse ? rp.T : (rp.T + FW * KS - 1) / (FW * KS);
   const int nshared = (int)(items < cap ? items : cap);
   hipLaunchKernelGGL(kern, dim3(nroute + nshared), dim3(NT), lds, stream, rp, q, nroute);
   return hipGetLastError();

@@ -98,7 +98,9 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
   const int nt_s = p.n_shared ? p.Nout_s / fcols : 0;
 
   // ---- items per active expert = token tiles x feature tiles; prefix sums
-  for (int e = tid; e <= E; e += NT) s_off[e] = p.expert_offset[e];
+  // compact layout: offsets [E+1]; masked layout: counts [E] (rows of
+  // expert e start at e*T)
+  for (int e = tid; e <= E; e += NT) s_off[e] = p.masked ? (e < E ? p.expert_offset[e] : 0) : p.expert_offset[e];
   __syncthreads();
   {
     const int per = (E + NT - 1) / NT;
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
       if (e < E) {
-        const int n = s_off[e + 1] - s_off[e];
+        const int n = p.masked ? s_off[e] : s_off[e + 1] - s_off[e];
         if (n > 0) { ++cnt; items += ((n + BN - 1) / BN) * nt_r; }
       }
     }
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
       if (e < E) {
-        const int n = s_off[e + 1] - s_off[e];
+        const int n = p.masked ? s_off[e] : s_off[e + 1] - s_off[e];
         if (n > 0) {
           s_grp[pc] = e;
           s_pre[pc] = pi;
@@ -163,8 +165,9 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
       const int a = __builtin_amdgcn_readfirstlane(lo);
       const int g = __builtin_amdgcn_readfirstlane(s_grp[a]);
       local = item - __builtin_amdgcn_readfirstlane(s_pre[a]);
-      it.rows0 = __builtin_amdgcn_readfirstlane(s_off[g]);
-      it.nrows = __builtin_amdgcn_readfirstlane(s_off[g + 1]) - it.rows0;
+      it.rows0 = p.masked ? g * p.T : __builtin_amdgcn_readfirstlane(s_off[g]);
+      it.nrows = p.masked ? __builtin_amdgcn_readfirstlane(s_off[g])
+                          : __builtin_amdgcn_readfirstlane(s_off[g + 1]) - it.rows0;
       mt = (it.nrows + BN - 1) / BN;
       it.K = p.K_r;
       it.Nout = p.Nout_r;

@@ -36,8 +36,14 @@ moe_status check_config(const moe_config* c) {
   const int mult = w == MOE_F32 ? 64 : w == MOE_BF16 ? 128 : 256;
   if (c->d_model % mult || c->d_ff % mult) return MOE_ERR_UNSUPPORTED;
   if (c->num_shared && c->d_ff_shared % mult) return MOE_ERR_UNSUPPORTED;
+  if (c->masked_layout != 0 && c->masked_layout != 1) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
+
+bool masked(const moe_config* c) { return c->masked_layout == 1; }
+
+// routed rows of every per-row buffer: T*k (compact) or E*T (masked)
+int64_t routed_rows(const moe_config* c, int64_t T) { return masked(c) ? T * c->num_experts : T * c->top_k; }
 
 bool fp8(const moe_config* c) { return c->weight_dtype == MOE_FP8_E4M3; }
 
@@ -45,8 +51,11 @@ bool fp8(const moe_config* c) { return c->weight_dtype == MOE_FP8_E4M3; }
 int recv_dtype(const moe_config* c) { return fp8(c) ? MOE_FP8_E4M3 : c->act_dtype; }
 
 int64_t dispatch_rows(const moe_config* c, int64_t T) {
-  return T * c->top_k + ((fp8(c) && c->num_shared) ? T : 0);
+  return routed_rows(c, T) + ((fp8(c) && c->num_shared) ? T : 0);
 }
+
+// row indices are int32 (row_of)
+bool rows_fit(const moe_config* c, int64_t T) { return dispatch_rows(c, T) <= 0x7FFFFFFF; }
 
 struct FfnLayout {
   size_t h, h_scale, hs, hs_scale, total;
@@ -55,7 +64,7 @@ struct FfnLayout {
 FfnLayout ffn_layout(const moe_config* c, int64_t T) {
   FfnLayout L{};
   const size_t eb = elem_bytes(recv_dtype(c));
-  const size_t rows = (size_t)T * c->top_k;
+  const size_t rows = (size_t)routed_rows(c, T);
   size_t o = 0;
   L.h = o;
   o = align256(o + rows * c->d_ff * eb);
@@ -89,7 +98,7 @@ LayerLayout layer_layout(const moe_config* c, int64_t T) {
   L.recv = o;   o = align256(o + rows * d * elem_bytes(recv_dtype(c)));
   L.recv_scale = o;
   if (fp8(c)) o = align256(o + rows * (d / 128) * sizeof(float));
-  L.eout = o;   o = align256(o + tk * d * sizeof(float));
+  L.eout = o;   o = align256(o + (size_t)routed_rows(c, T) * d * sizeof(float));
   L.sout = o;
   if (c->num_shared) o = align256(o + (size_t)T * d * sizeof(float));
   L.ffn = o;    o = align256(o + ffn_layout(c, T).total);
@@ -111,6 +120,15 @@ RouteParams route_params(const moe_config* c, int32_t T, const float* logits, co
   return p;
 }
 
+// the router also writes every token into its masked-layout rows
+void fuse_dispatch(RouteParams& p, const moe_config* c, const void* x, void* recv, float* recv_scale,
+                   int32_t* row_of) {
+  p.fuse = 1; p.d = c->d_model; p.act_dtype = c->act_dtype;
+  p.quant = fp8(c) ? 1 : 0;
+  p.shared_rows = (fp8(c) && c->num_shared) ? 1 : 0;
+  p.x = x; p.recv = recv; p.recv_scale = recv_scale; p.row_of = row_of;
+}
+
 moe_status route_impl(const moe_config* c, int32_t T, const float* logits, const float* bias, int32_t* idx,
                       float* w, int32_t* count, int32_t* ticket, hipStream_t s) {
   return hip_status(launch_route(route_params(c, T, logits, bias, idx, w, count, ticket), s));
@@ -123,6 +141,8 @@ moe_status dispatch_impl(const moe_config* c, int32_t T, const void* x, const in
   p.T = T; p.E = c->num_experts; p.k = c->top_k; p.d = c->d_model; p.act_dtype = c->act_dtype;
   p.quant = fp8(c) ? 1 : 0;
   p.shared_rows = (fp8(c) && c->num_shared) ? 1 : 0;
+  p.masked = masked(c) ? 1 : 0;
+  p.routed_rows = (int)routed_rows(c, T);
   p.x = x; p.topk_idx = idx; p.expert_count = count; p.ticket = ticket; p.recv = recv; p.recv_scale = recv_scale;
   p.expert_offset = offset; p.row_of = row_of;
   return hip_status(launch_dispatch(p, s));
@@ -135,7 +155,7 @@ FfnParams gate_up_params(const moe_config* c, int32_t T, const void* recv, const
   const bool q = fp8(c);
   const int d = c->d_model, F = c->d_ff, Fs = c->d_ff_shared, ns = c->num_shared;
   FfnParams a{};
-  a.E = c->num_experts; a.T = T; a.expert_offset = offset; a.n_shared = ns;
+  a.E = c->num_experts; a.T = T; a.expert_offset = offset; a.masked = masked(c) ? 1 : 0; a.n_shared = ns;
   a.tiles_r = F / 16; a.tiles_s = ns ? Fs / 16 : 0;
   a.act = static_cast<const uint8_t*>(recv); a.act_scale = recv_scale;
   a.w = static_cast<const uint8_t*>(W->w13); a.w_scale = W->w13_scale;
@@ -143,8 +163,8 @@ FfnParams gate_up_params(const moe_config* c, int32_t T, const void* recv, const
   a.out = base + L.h; a.out_scale = q ? reinterpret_cast<float*>(base + L.h_scale) : nullptr;
   if (ns) {
     if (q) {
-      a.s_act = static_cast<const uint8_t*>(recv) + (size_t)T * c->top_k * d;
-      a.s_act_scale = recv_scale + (size_t)T * c->top_k * (d / 128);
+      a.s_act = static_cast<const uint8_t*>(recv) + (size_t)routed_rows(c, T) * d;
+      a.s_act_scale = recv_scale + (size_t)routed_rows(c, T) * (d / 128);
     } else {
       a.s_act = static_cast<const uint8_t*>(x);
     }
@@ -162,7 +182,7 @@ FfnParams down_params(const moe_config* c, int32_t T, const int32_t* offset, con
   const bool q = fp8(c);
   const int d = c->d_model, F = c->d_ff, Fs = c->d_ff_shared, ns = c->num_shared;
   FfnParams b{};
-  b.E = c->num_experts; b.T = T; b.expert_offset = offset; b.n_shared = ns;
+  b.E = c->num_experts; b.T = T; b.expert_offset = offset; b.masked = masked(c) ? 1 : 0; b.n_shared = ns;
   b.tiles_r = d / 16; b.tiles_s = ns ? d / 16 : 0;
   b.act = base + L.h; b.act_scale = q ? reinterpret_cast<const float*>(base + L.h_scale) : nullptr;
   b.w = static_cast<const uint8_t*>(W->w2); b.w_scale = W->w2_scale;
@@ -263,7 +283,7 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const float* logits, cons
                      float* topk_w, int32_t* expert_count, int32_t* ticket, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || !rows_fit(cfg, T)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w || !expert_count || !ticket) return MOE_ERR_INVALID_ARG;
   if (!all_aligned(logits, topk_idx, topk_w, expert_count, ticket) || (bias && !aligned16(bias)))
@@ -276,14 +296,34 @@ moe_status moe_dispatch(const moe_config* cfg, int32_t T, const void* x, const i
                         int32_t* expert_offset, int32_t* row_of, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || !rows_fit(cfg, T)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
-  if (!x || !topk_idx || !expert_count || !ticket || !recv || !expert_offset || !row_of) return MOE_ERR_INVALID_ARG;
+  if (!x || !topk_idx || !expert_count || !ticket || !recv || !row_of) return MOE_ERR_INVALID_ARG;
+  if (!masked(cfg) && !expert_offset) return MOE_ERR_INVALID_ARG;
   if (fp8(cfg) && !recv_scale) return MOE_ERR_INVALID_ARG;
-  if (!all_aligned(x, topk_idx, expert_count, ticket, recv, expert_offset, row_of)) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(x, topk_idx, expert_count, ticket, recv, row_of) || (expert_offset && !aligned16(expert_offset)))
+    return MOE_ERR_INVALID_ARG;
   if (recv_scale && !aligned16(recv_scale)) return MOE_ERR_INVALID_ARG;
   return dispatch_impl(cfg, T, x, topk_idx, expert_count, ticket, recv, recv_scale, expert_offset, row_of,
                        (hipStream_t)stream);
+}
+
+moe_status moe_route_dispatch(const moe_config* cfg, int32_t T, const float* logits, const float* bias,
+                              const void* x, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                              int32_t* ticket, void* recv, float* recv_scale, int32_t* row_of, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!masked(cfg)) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || !rows_fit(cfg, T)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !x || !topk_idx || !topk_w || !expert_count || !recv || !row_of) return MOE_ERR_INVALID_ARG;
+  if (fp8(cfg) && !recv_scale) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(logits, x, topk_idx, topk_w, expert_count, recv, row_of) || (bias && !aligned16(bias)) ||
+      (ticket && !aligned16(ticket)) || (recv_scale && !aligned16(recv_scale)))
+    return MOE_ERR_INVALID_ARG;
+  RouteParams p = route_params(cfg, T, logits, bias, topk_idx, topk_w, expert_count, ticket);
+  fuse_dispatch(p, cfg, x, recv, fp8(cfg) ? recv_scale : nullptr, row_of);
+  return hip_status(launch_route(p, (hipStream_t)stream));
 }
 
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t T, const void* recv, const float* recv_scale,
@@ -291,7 +331,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t T, const void* recv, co
                           float* shared_out, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || !rows_fit(cfg, T)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if ((st = check_weights(cfg, w)) != MOE_OK) return st;
   if (!recv || !expert_offset || !expert_out || !ws) return MOE_ERR_INVALID_ARG;
@@ -309,7 +349,7 @@ moe_status moe_ffn_gate_up(const moe_config* cfg, int32_t T, const void* recv, c
                            size_t ws_bytes, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || !rows_fit(cfg, T)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if ((st = check_weights(cfg, w)) != MOE_OK) return st;
   if (!recv || !expert_offset || !ws) return MOE_ERR_INVALID_ARG;
@@ -325,7 +365,7 @@ moe_status moe_ffn_down(const moe_config* cfg, int32_t T, const int32_t* expert_
                         const void* ws, size_t ws_bytes, float* expert_out, float* shared_out, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || !rows_fit(cfg, T)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if ((st = check_weights(cfg, w)) != MOE_OK) return st;
   if (!expert_offset || !ws || !expert_out) return MOE_ERR_INVALID_ARG;
@@ -341,7 +381,7 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
                        void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || !rows_fit(cfg, T)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!expert_out || !row_of || !topk_w || !y || !expert_count) return MOE_ERR_INVALID_ARG;
   if (!all_aligned(expert_out, row_of, topk_w, y, expert_count) || (shared_out && !aligned16(shared_out)))
@@ -353,7 +393,7 @@ moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const floa
                      const moe_weights* w, void* y, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || !rows_fit(cfg, T)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if ((st = check_weights(cfg, w)) != MOE_OK) return st;
   if (!x || !logits || !y || !ws) return MOE_ERR_INVALID_ARG;
@@ -373,6 +413,28 @@ moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const floa
   float* eout = reinterpret_cast<float*>(b + L.eout);
   float* sout = cfg->num_shared ? reinterpret_cast<float*>(b + L.sout) : nullptr;
   void* ffn_ws = b + L.ffn;
+  if (masked(cfg)) {
+    // route and dispatch in one launch; the GEMMs read the counters in
+    // place of offsets
+    RouteParams rp = route_params(cfg, T, logits, bias, idx, tw, count, nullptr);
+    fuse_dispatch(rp, cfg, x, recv, recv_scale, row_of);
+    if (cfg->num_shared && !use_tiled(cfg, T)) {
+      const FfnParams a = gate_up_params(cfg, T, recv, recv_scale, count, w, x, ffn_ws);
+      if (route_shared_supported(a, cfg->weight_dtype)) {
+        if ((st = hip_status(launch_route_shared(rp, a, cfg->weight_dtype, s))) != MOE_OK) return st;
+        FfnParams routed = a;
+        routed.n_shared = 0;
+        if ((st = hip_status(launch_ffn(routed, cfg->weight_dtype, true, (long long)T * cfg->top_k,
+                                        max_groups_of(cfg, T), s))) != MOE_OK)
+          return st;
+        if ((st = down_impl(cfg, T, count, w, ffn_ws, eout, sout, s)) != MOE_OK) return st;
+        return combine_impl(cfg, T, eout, row_of, tw, sout, y, count, s);
+      }
+    }
+    if ((st = hip_status(launch_route(rp, s))) != MOE_OK) return st;
+    if ((st = ffn_impl(cfg, T, recv, recv_scale, count, w, x, eout, sout, ffn_ws, s)) != MOE_OK) return st;
+    return combine_impl(cfg, T, eout, row_of, tw, sout, y, count, s);
+  }
   if (cfg->num_shared && !use_tiled(cfg, T)) {
     // The shared expert needs no routing: its gate/up pass streams its
     // weights in the router's launch, and the routed pass follows dispatch.

@@ -13,13 +13,23 @@ struct RouteParams {
   int* topk_idx;
   float* topk_w;
   int* expert_count;
-  int* ticket;
+  int* ticket;  // may be NULL when fuse is set
+  // fuse: also write the token into its masked-layout rows (row e*T +
+  // ticket; E4M3 codes and scales when quant, plus row E*T + t for the
+  // shared expert when shared_rows) and row_of
+  int fuse, d, act_dtype, quant, shared_rows;
+  const void* x;
+  void* recv;
+  float* recv_scale;
+  int* row_of;
 };
 
 struct DispatchParams {
   int T, E, k, d, act_dtype;
   int quant;        // write E4M3 codes + per-128 scales
-  int shared_rows;  // also write rows T*k + t for the shared expert (quant only)
+  int shared_rows;  // also write rows routed_rows + t for the shared expert (quant only)
+  int masked;       // masked layout: row e*T + ticket, no offsets
+  int routed_rows;  // T*k (compact) or E*T (masked)
   const void* x;
   const int* topk_idx;
   const int* expert_count;
@@ -37,7 +47,10 @@ struct DispatchParams {
 // weight matrix and write silu(gate) * up; plain passes write the product.
 struct FfnParams {
   int E, T;
-  const int* expert_offset;  // [E+1]
+  // compact layout: [E+1] offsets, expert e's rows are [off[e], off[e+1]);
+  // masked layout: [E] counts, expert e's rows are [e*T, e*T + cnt[e])
+  const int* expert_offset;
+  int masked;
   int n_shared;
   int tiles_r, tiles_s;
   // routed experts: activation rows [expert_offset[e], expert_offset[e+1])

@@ -17,14 +17,24 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
   route_body<KPL, 4>(p, blockIdx.x, smem);
 }
 
+template <int KPL>
+__global__ __launch_bounds__(256) void route_dispatch_kernel(RouteParams p) {
+  extern __shared__ float smem[];
+  route_dispatch_block<KPL>(p, blockIdx.x, smem);
+}
+
+// Four tokens per workgroup, one per wave; with the masked-layout write
+// (p.fuse) one token per workgroup, whose four waves share the copy.
 hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
   const int kpl_needed = (p.E + 63) / 64;
-  const int blocks = (p.T + 3) / 4;
-  const size_t lds = 4 * (size_t)route_lds_floats(p.E) * sizeof(float);
-#define MOE_ROUTE_CASE(K)                                                                \
-  if (kpl_needed <= K) {                                                                 \
-    hipLaunchKernelGGL(route_kernel<K>, dim3(blocks), dim3(256), lds, stream, p);        \
-    return hipGetLastError();                                                            \
+  const int nw = p.fuse ? 1 : 4;
+  const int blocks = (p.T + nw - 1) / nw;
+  const size_t lds = nw * (size_t)route_lds_floats(p.E) * sizeof(float);
+#define MOE_ROUTE_CASE(K)                                                                            \
+  if (kpl_needed <= K) {                                                                             \
+    if (p.fuse) hipLaunchKernelGGL(route_dispatch_kernel<K>, dim3(blocks), dim3(256), lds, stream, p); \
+    else hipLaunchKernelGGL(route_kernel<K>, dim3(blocks), dim3(256), lds, stream, p);               \
+    return hipGetLastError();                                                                        \
   }
   MOE_ROUTE_CASE(1)
   MOE_ROUTE_CASE(2)
@@ -74,10 +84,12 @@ __device__ void block_offsets(const int* cnt, int E, int* off, int* wsum) {
   __syncthreads();
 }
 
-// Grid (T, column blocks).  Plain rows: a block copies 4096 bytes of its
-// token (256 threads x 16 B); E4M3 rows: a block quantises four 128-column
-// blocks (one per wave).  The token's bytes and its slot tickets are loaded
-// before the offsets scan so that their latency overlaps it.
+// Grid (T, column blocks).  Compact layout: rows follow from the offsets
+// scan; masked layout: row = expert * T + ticket, no scan.  Plain rows: a
+// block copies 4096 bytes of its token (256 threads x 16 B); E4M3 rows: a
+// block quantises four 128-column blocks (one per wave).  The token's bytes
+// and its slot tickets are loaded before the offsets scan so that their
+// latency overlaps it.
 template <int ACT, bool QUANT>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
   __shared__ int off[1025];
@@ -108,15 +120,17 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
     if (blk < nb)
       pair = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.x) + (size_t)t * d)[blk * 64 + lane];
   }
-  block_offsets(p.expert_count, p.E, off, wsum);
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int e = tid; e <= p.E; e += 256) p.expert_offset[e] = off[e];
+  if (!p.masked) {  // uniform: the scan's barriers are met by every thread
+    block_offsets(p.expert_count, p.E, off, wsum);
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+      for (int e = tid; e <= p.E; e += 256) p.expert_offset[e] = off[e];
+  }
   if (tid < k) {
-    const int r = off[my_e] + my_ticket;
+    const int r = p.masked ? my_e * p.T + my_ticket : off[my_e] + my_ticket;
     rows[tid] = r;
     if (blockIdx.y == 0) p.row_of[(size_t)t * k + tid] = r;
   }
-  if (tid == 0) rows[k] = QUANT && p.shared_rows ? k * p.T + t : -1;
+  if (tid == 0) rows[k] = QUANT && p.shared_rows ? p.routed_rows + t : -1;
   __syncthreads();
   const int nrows = (QUANT && p.shared_rows) ? k + 1 : k;
 

@@ -32,9 +32,11 @@ __device__ __forceinline__ uint32_t ord(float f) {
 __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
 
 // Routes token bid * NW + w with wave w of an NW-wave block; smem holds
-// route_lds_floats(E) floats per wave.
+// route_lds_floats(E) floats per wave.  Returns, in lane j < k, the
+// masked-layout row of the token's slot j (when p.fuse; 0 otherwise), and -1
+// in every lane when the token is past T.
 template <int KPL, int NW>
-__device__ __forceinline__ void route_body(const RouteParams& p, int bid, float* smem) {
+__device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* smem) {
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int t = bid * NW + wid;
@@ -50,7 +52,7 @@ __device__ __forceinline__ void route_body(const RouteParams& p, int bid, float*
   int* ce = reinterpret_cast<int*>(cu + 64);
   int* oe = ce + 64;
   float* os = reinterpret_cast<float*>(oe + 64);
-  if (t >= p.T) return;  // uniform per wave; no block barrier is used below
+  if (t >= p.T) return -1;  // uniform per wave; no block barrier is used below
 
   const float* lg = p.logits + (size_t)t * E;
   float key[KPL];
@@ -242,11 +244,70 @@ __device__ __forceinline__ void route_body(const RouteParams& p, int bid, float*
   }
   w *= p.routed_scale;
 
+  int my_row = 0;
   if (lane < k) {
     const size_t o = (size_t)t * k + lane;
     p.topk_idx[o] = my_idx;
     p.topk_w[o] = w;
-    p.ticket[o] = atomicAdd(p.expert_count + my_idx, 1);
+    const int tk = atomicAdd(p.expert_count + my_idx, 1);
+    if (p.ticket) p.ticket[o] = tk;
+    if (p.fuse) {
+      my_row = my_idx * p.T + tk;
+      p.row_of[o] = my_row;
+    }
+  }
+  return my_row;
+}
+
+// Masked layout, one token per 256-thread workgroup: wave 0 routes it, then
+// the whole workgroup writes it into the k rows its tickets reserved ("One-
+// Sided Expert-Parallel All-to-All", abstract: tokens are pushed straight
+// into expert-grouped buffers).  Plain rows are copied 16 bytes per thread;
+// E4M3 rows are quantised per 128 columns (one block per wave, two values
+// per lane) with the same arithmetic as the dispatch kernel, and also written
+// to row E*T + t for the shared expert when p.shared_rows.  smem holds
+// route_lds_floats(E) floats.
+template <int KPL>
+__device__ __forceinline__ void route_dispatch_block(const RouteParams& p, int t, float* smem) {
+  __shared__ int rows_s[65];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int NWAVE = 4;
+  if (wid == 0) {
+    const int my_row = route_body<KPL, 1>(p, t, smem);
+    if (lane < p.k) rows_s[lane] = my_row;
+    if (lane == 0) rows_s[p.k] = p.E * p.T + t;
+  }
+  __syncthreads();
+  const int k = p.k, d = p.d;
+  if (!p.quant) {
+    const int eb = p.act_dtype == MOE_F32 ? 4 : 2;
+    const int pieces = d * eb / 16;
+    const i32x4_t* src = reinterpret_cast<const i32x4_t*>(static_cast<const uint8_t*>(p.x) + (size_t)t * d * eb);
+    for (int c = tid; c < pieces; c += 64 * NWAVE) {
+      const i32x4_t v = src[c];
+      for (int j = 0; j < k; ++j)
+        reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows_s[j] * d * eb)[c] = v;
+    }
+    return;
+  }
+  const int nb = d / 128;
+  const int nrows = p.shared_rows ? k + 1 : k;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.x) + (size_t)t * d);
+  for (int b = wid; b < nb; b += NWAVE) {  // uniform per wave
+    const uint32_t pair = src[b * 64 + lane];
+    const float v0 = bf16_bits_to_f32(pair & 0xFFFFu), v1 = bf16_bits_to_f32(pair >> 16);
+    float amax = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    const uint32_t c0 = f32_to_e4m3(v0 / scale), c1 = f32_to_e4m3(v1 / scale);
+    const uint16_t codes = (uint16_t)(c0 | (c1 << 8));
+    for (int j = 0; j < nrows; ++j) {
+      const int r = rows_s[j];
+      uint8_t* dst = static_cast<uint8_t*>(p.recv) + (size_t)r * d;
+      reinterpret_cast<uint16_t*>(dst + b * 128)[lane] = codes;
+      if (lane == 0) p.recv_scale[(size_t)r * nb + b] = scale;
+    }
   }
 }
 

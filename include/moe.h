@@ -89,6 +89,13 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
  *   token per 128 columns inside the layer; weights carry 128x128 block
  *   scales).
  *   Size rules: d, F, Fs multiples of 64 (F32), 128 (BF16) or 256 (FP8).
+ *   masked_layout: 0 = compact dispatch layout (expert e owns rows
+ *             [expert_offset[e], expert_offset[e+1]) of T*k rows, offsets
+ *             from a scan of the counters); 1 = masked layout (expert e owns
+ *             rows [e*T, e*T + expert_count[e]) of E*T rows: a token's row
+ *             follows from its ticket alone, so the router can write it,
+ *             with no scan and no dispatch launch).  Same results, more
+ *             memory: every per-row buffer has E*T rows instead of T*k.
  */
 typedef struct {
   int32_t num_experts;
@@ -104,6 +111,7 @@ typedef struct {
   float routed_scale;
   int32_t act_dtype;    /* moe_dtype */
   int32_t weight_dtype; /* moe_dtype */
+  int32_t masked_layout; /* 0 compact, 1 masked */
 } moe_config;
 
 /*
@@ -128,10 +136,12 @@ typedef struct {
   const float* ws2_scale;
 } moe_weights;
 
-/* Row count of the dispatch buffer for T tokens: T*k routed rows, plus T rows
- * holding the quantised tokens for the shared expert when weight_dtype is
- * FP8 and num_shared is 1 (in the bf16 and f32 paths the shared expert reads
- * x directly). */
+/* Row count of the dispatch buffer for T tokens: the routed rows (T*k in
+ * the compact layout, E*T in the masked one), plus T rows holding the
+ * quantised tokens for the shared expert when weight_dtype is FP8 and
+ * num_shared is 1 (in the bf16 and f32 paths the shared expert reads x
+ * directly).  The routed row count also sizes expert_out and row_of's
+ * values. */
 int64_t moe_dispatch_rows(const moe_config* cfg, int32_t T);
 
 /* Bytes of device workspace moe_expert_ffn needs for up to max_tokens tokens
@@ -166,14 +176,18 @@ moe_status moe_route(const moe_config* cfg, int32_t T, const float* logits, cons
  *   x             [T][d] act_dtype
  *   topk_idx, expert_count, ticket: as left by moe_route
  *   recv          [moe_dispatch_rows][d] out: act_dtype, or E4M3 bytes when
- *                 weight_dtype is FP8.  Expert e owns rows
+ *                 weight_dtype is FP8.  Compact layout: expert e owns rows
  *                 [expert_offset[e], expert_offset[e+1]); token t's slot j
  *                 lands in row expert_offset[topk_idx[t][j]] + ticket[t][j].
- *                 FP8 + shared expert: row T*k + t holds token t.
+ *                 Masked layout: row topk_idx[t][j] * T + ticket[t][j].
+ *                 FP8 + shared expert: the row after the routed rows, plus
+ *                 t, holds token t.
  *   recv_scale    [moe_dispatch_rows][d/128] fp32 out (FP8 only, else NULL):
  *                 per-row, per-128-column scale; code = E4M3(x / scale) with
  *                 scale = amax / 448 (1 when amax = 0), nearest-even, saturating
  *   expert_offset [E+1] int32 out: exclusive prefix sum of expert_count
+ *                 (compact layout; not written, and may be NULL, in the
+ *                 masked layout)
  *   row_of        [T][k] int32 out: the row of token t's slot j
  */
 moe_status moe_dispatch(const moe_config* cfg, int32_t T, const void* x, const int32_t* topk_idx,
@@ -181,10 +195,30 @@ moe_status moe_dispatch(const moe_config* cfg, int32_t T, const void* x, const i
                         float* recv_scale, int32_t* expert_offset, int32_t* row_of, void* stream);
 
 /*
+ * moe_route_dispatch: moe_route and moe_dispatch in one launch, for the
+ * masked layout (masked_layout must be 1; MOE_ERR_INVALID_ARG otherwise).
+ * "One-Sided Expert-Parallel All-to-All" (abstract): a token reserves its
+ * slot with an atomic add on the expert's counter and is written straight
+ * into that slot; with the masked layout the slot's row is known as soon as
+ * the ticket is, so the routing wave writes the token itself.
+ *   logits, bias, topk_idx, topk_w, expert_count: as for moe_route
+ *   ticket        [T][k] int32 out, or NULL when the caller does not need it
+ *   x, recv, recv_scale, row_of: as for moe_dispatch (masked layout)
+ * Results equal moe_route followed by moe_dispatch.
+ */
+moe_status moe_route_dispatch(const moe_config* cfg, int32_t T, const float* logits, const float* bias,
+                              const void* x, int32_t* topk_idx, float* topk_w, int32_t* expert_count,
+                              int32_t* ticket, void* recv, float* recv_scale, int32_t* row_of,
+                              void* stream);
+
+/*
  * moe_expert_ffn: grouped SwiGLU experts over the dispatch buffer, read in
  * place, and the shared expert over x.  Experts with no rows read none of
  * their weights.
- *   recv, recv_scale, expert_offset: as left by moe_dispatch
+ *   recv, recv_scale, expert_offset: as left by moe_dispatch.  In the
+ *                masked layout pass expert_count (as left by moe_route or
+ *                moe_route_dispatch) in place of expert_offset: expert e's
+ *                rows are [e*T, e*T + expert_count[e]).
  *   w            expert weights (host struct of device pointers)
  *   x            [T][d] act_dtype (shared expert input; may be NULL when
  *                num_shared == 0)
@@ -229,7 +263,8 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
  * moe_layer: route -> dispatch -> expert FFN (+ shared expert) -> combine in
  * one call, every intermediate carved from ws (>= moe_workspace_size(cfg, T)
  * bytes, zero-filled once by the caller).  Launches only; no host sync, so
- * the sequence can be captured in a HIP graph.
+ * the sequence can be captured in a HIP graph.  With the masked layout the
+ * route and dispatch steps are one launch (moe_route_dispatch).
  */
 moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const float* logits,
                      const float* bias, const moe_weights* w, void* y, void* ws, size_t ws_bytes,

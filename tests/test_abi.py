@@ -117,3 +117,31 @@ def test_workspace_sizes_grow_with_tokens(M):
     assert M.moe_dispatch_rows(cfg, 128) == 1024
     assert M.moe_dispatch_rows(dsv3(M, weight_dtype="fp8"), 128) == 1024 + 128
     assert M.moe_dispatch_rows(dsv3(M, weight_dtype="fp8", num_shared=0), 128) == 1024
+
+
+def test_masked_layout_sizes_and_argument_checks(M):
+    cm = dsv3(M, masked=True)
+    # expert e owns rows [e*T, e*T + count): E*T routed rows (+ T shared rows on the fp8 path)
+    assert M.moe_dispatch_rows(cm, 128) == 256 * 128
+    assert M.moe_dispatch_rows(dsv3(M, weight_dtype="fp8", masked=True), 128) == 256 * 128 + 128
+    assert M.moe_workspace_size(cm, 128) > M.moe_workspace_size(dsv3(M), 128)
+    assert M.moe_ffn_workspace_size(cm, 128) > M.moe_ffn_workspace_size(dsv3(M), 128)
+    bad = dsv3(M)
+    bad.masked_layout = 2
+    assert M.moe_workspace_size(bad, 16) == 0
+    # the fused route + dispatch exists for the masked layout only
+    with pytest.raises(M.MoeError) as e:
+        M.moe_route_dispatch(dsv3(M), 4, 16, None, 16, 16, 16, 16, None, 16, None, 16, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:  # recv missing
+        M.moe_route_dispatch(cm, 4, 16, None, 16, 16, 16, 16, None, None, None, 16, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    M.moe_route_dispatch(cm, 0, None, None, None, None, None, None, None, None, None, None, stream=0)
+    # row indices are int32: E*T rows must fit
+    with pytest.raises(M.MoeError) as e:
+        M.moe_route_dispatch(cm, 1 << 23, 16, None, 16, 16, 16, 16, None, 16, None, 16, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    # the compact dispatch needs expert_offset; the masked one does not take it
+    with pytest.raises(M.MoeError) as e:
+        M.moe_dispatch(dsv3(M), 4, 16, 16, 16, 16, 16, None, None, 16, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG

@@ -237,18 +237,33 @@ def touched_experts(layer, b):
     return int((c > 0).sum()), c
 
 
-def measure(layer, b, steps, warmup, flush):
+def measure(layer, b, steps, warmup, flush, graph=False):
     import torch
     for _ in range(warmup):
         flush()
         run_layer(layer, b)
     torch.cuda.synchronize()
+    step = lambda: run_layer(layer, b)  # noqa: E731
+    if graph:
+        # the same moe_layer call captured once and replayed (its launches
+        # are fixed for a shape; the workspace counters return to zero)
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        with torch.cuda.stream(cs):
+            with torch.cuda.graph(g, stream=cs):
+                run_layer(layer, b)
+        torch.cuda.synchronize()
+        step = g.replay
+        for _ in range(warmup):
+            flush()
+            step()
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for s, e in ev:
         flush()
         s.record()
-        run_layer(layer, b)
+        step()
         e.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -322,6 +337,8 @@ def main():
     ap.add_argument("--tokens", default=None, help="override the token counts, e.g. 1,8,128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of moe_layer captured in a HIP graph instead of direct calls")
     ap.add_argument("--layout", choices=("compact", "masked"), default="compact",
                     help="dispatch layout: compact (T*k rows from a scan of the counters) or masked "
                          "(E*T rows, route and dispatch in one launch)")
@@ -375,14 +392,15 @@ def main():
             b = Batch(layer, wl, T)
             b_wl = wl
             D, counts = touched_experts(layer, b)
-            layer_us, ph, wall = measure(layer, b, args.steps, args.warmup, flush)
+            layer_us, ph, wall = measure(layer, b, args.steps, args.warmup, flush, graph=args.graph)
             nbytes, flops, wbytes = layer_work(b_wl, T, D)
             med = float(np.median(layer_us))
             gu_bytes, gu_flops = gate_up_work(b_wl, T, D)
             gu_us = float(ph[:, 2].mean())
             peak_t = MFMA_PEAK_TFLOPS[b_wl.weight_dtype]
             ent = {
-                "workload": WORKLOAD_NAMES[name], "tokens": T, "layout": args.layout, "touched_experts": D,
+                "workload": WORKLOAD_NAMES[name], "tokens": T, "layout": args.layout,
+                "launch": "hip graph replay" if args.graph else "direct", "touched_experts": D,
                 "layer_us_median": round(med, 2), "layer_us_p10": round(float(np.percentile(layer_us, 10)), 2),
                 "layer_us_p90": round(float(np.percentile(layer_us, 90)), 2),
                 "tokens_per_s": round(T / med * 1e6, 1),
@@ -432,6 +450,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded SplitMix64/Box-Muller inputs of the workload's shapes; random weights)",
         "config": {"workload": ent["workload"], "tokens": ent["tokens"], "layout": ent["layout"],
+                   "launch": ent["launch"],
                    "cache": "cold (1 GiB read before each step)"},
     }
     if gu_us:

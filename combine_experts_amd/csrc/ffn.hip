@@ -630,11 +630,19 @@ static hipError_t launch_rs(const RouteParams& rp, const FfnParams& q, long long
   auto kern = route_shared_kernel<KPL, FW, KS>;
   constexpr int NT = 64 * FW * KS;
   const size_t lds = (size_t)(FW * KS) * route_lds_floats(rp.E) * sizeof(float);
-  int dev = 0, n = 0, c = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, lds) != hipSuccess || n < 1) n = 1;
-  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 256;
-  const long long cap = (long long)n * c;
+  // workgroups per CU for the largest routing LDS (E = 1024), constant per
+  // kernel and device model
+  static int per_cu = -1, cus = -1;
+  if (per_cu < 0) {
+    int dev = 0, n = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const size_t lds_max = (size_t)(FW * KS) * route_lds_floats(1024) * sizeof(float);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, lds_max) != hipSuccess || n < 1) n = 1;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 256;
+    per_cu = n;
+    cus = c;
+  }
+  const long long cap = (long long)per_cu * cus;
   const int nroute = rp.fuse ? rp.T : (rp.T + FW * KS - 1) / (FW * KS);
   const int nshared = (int)(items < cap ? items : cap);
   hipLaunchKernelGGL(kern, dim3(nroute + nshared), dim3(NT), lds, stream, rp, q, nroute);

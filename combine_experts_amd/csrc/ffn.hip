@@ -690,11 +690,22 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
     if (gated) return launch_plan<MOE_F32, true, MOE_F32>(q, pl, items, stream);
     return launch_plan<MOE_F32, false, MOE_F32>(q, pl, items, stream);
   }
+  // every wave of a workgroup walks the same number of steps per item
+  const bool even = (q.K_r / step) % pl.ks == 0 && (!q.n_shared || (q.K_s / step) % pl.ks == 0);
   if (wdtype == MOE_BF16) {
+    // bf16 tiles are shared only between column waves of items with 16 or
+    // more steps: measured at 128 tokens, 128 experts: gate/up (16 steps)
+    // 143.0 -> 141.5 us, but the 6-step down pass 80.4 -> 84.2 us; 256
+    // experts: down (16 steps) 941 -> 916 us
+    int steps = q.K_r / step;
+    if (q.n_shared && q.K_s / step < steps) steps = q.K_s / step;
+    if (pl.fw >= 2 && steps >= 16 && even) {
+      if (gated) return launch_plan<MOE_BF16, true, MOE_BF16, 1, true, true>(q, pl, items, stream);
+      return launch_plan<MOE_BF16, false, MOE_F32, 1, true, true>(q, pl, items, stream);
+    }
     if (gated) return launch_plan<MOE_BF16, true, MOE_BF16>(q, pl, items, stream);
     return launch_plan<MOE_BF16, false, MOE_F32>(q, pl, items, stream);
   }
-  const bool even = (q.K_r / step) % pl.ks == 0 && (!q.n_shared || (q.K_s / step) % pl.ks == 0);
   if (wide) {
     // The waves of a workgroup share each step's 32-row activation tile
     // through LDS (measured upper bound, with the activation loads removed

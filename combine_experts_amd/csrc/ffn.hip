@@ -654,6 +654,7 @@ static hipError_t launch_plan(const FfnParams& p, const Plan& pl, long long item
   MOE_FFN_CASE(1, 4)
   MOE_FFN_CASE(1, 2)
   MOE_FFN_CASE(1, 1)
+  MOE_FFN_CASE(8, 1)
   MOE_FFN_CASE(4, 1)
   MOE_FFN_CASE(2, 2)
   MOE_FFN_CASE(2, 1)
@@ -665,13 +666,7 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
                       hipStream_t stream) {
   const int step = wdtype == MOE_F32 ? 64 : wdtype == MOE_BF16 ? 128 : 256;
   if (p.K_r / step < 1 || (p.n_shared && p.K_s / step < 1)) return hipErrorInvalidValue;
-  const Plan pl = plan_of(p, step, gated, wdtype);
-  // a work item covers FW waves' columns; a plain-pass wave covers two tiles
-  const int per_item = pl.fw * (gated ? 1 : 2);
-  FfnParams q = p;
-  q.tiles_r = p.tiles_r / per_item;
-  q.tiles_s = p.tiles_s / per_item;
-  if (q.tiles_r * per_item != p.tiles_r || q.tiles_s * per_item != p.tiles_s) return hipErrorInvalidValue;
+  Plan pl = plan_of(p, step, gated, wdtype);
   // E4M3 batches with many rows per expert (T k >= 12 E) use 32-row chunks:
   // each weight tile is then streamed once per 32 rows instead of once per 16
   // (measured at 512 tokens x 8 of 256 experts: gate/up 2036 -> 1792 us; at
@@ -679,6 +674,26 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
   // leave no registers for parked accumulators, so those walks finish each
   // item in line.
   const bool wide = wdtype == MOE_FP8_E4M3 && routed_rows >= 12LL * max_groups;
+#ifndef MOE_FFN_FW
+  // Once experts hold a few rows each, the E4M3 down pass does better with
+  // more column waves sharing each activation tile and no K-split.  Measured
+  // at 256 experts x 8 slots, down pass with (2, 2) / (4, 1) / (8, 1): 512
+  // tokens 782 / 710 / 686 us; 128 tokens 506 / 489 / 494 us; 32 tokens (one
+  // row per expert) 322 / 326 / 335 us.
+  if (!gated && wdtype == MOE_FP8_E4M3 && routed_rows >= 2LL * max_groups) {
+    for (const Plan w : {wide ? Plan{8, 1} : Plan{4, 1}, Plan{4, 1}})
+      if (p.tiles_r % (2 * w.fw) == 0 && p.tiles_s % (2 * w.fw) == 0) {
+        pl = w;
+        break;
+      }
+  }
+#endif
+  // a work item covers FW waves' columns; a plain-pass wave covers two tiles
+  const int per_item = pl.fw * (gated ? 1 : 2);
+  FfnParams q = p;
+  q.tiles_r = p.tiles_r / per_item;
+  q.tiles_s = p.tiles_s / per_item;
+  if (q.tiles_r * per_item != p.tiles_r || q.tiles_s * per_item != p.tiles_s) return hipErrorInvalidValue;
   const int CH = wide ? 32 : 16;
   // CH-row chunks over all groups: full chunks plus at most one partial
   // chunk per group (bounds the items, which sizes the grid)

@@ -42,6 +42,16 @@ ODD = {
     # d_model not a multiple of 256: the down pass takes 128-row weight tiles
     "tiled_narrow": WL["dsv3"].with_(name="tiled_narrow", num_experts=8, top_k=2, d_model=384, d_ff=256,
                                      d_ff_shared=384, n_group=2, topk_group=1),
+    # bf16 activation tiles shared through LDS or not: the gate/up pass has 17
+    # K-steps per item, which a 2-way K-split cannot divide (private tiles);
+    # the down pass has 16 (shared tiles)
+    "share_odd": WL["dsv3"].with_(name="share_odd", num_experts=8, top_k=2, d_model=2176, d_ff=2048,
+                                  d_ff_shared=2048, n_group=2, topk_group=1),
+    # E4M3 down pass with 9 K-steps: private tiles under a 2-way K-split (few
+    # rows per expert), shared by (4, 1) column waves with two or more rows
+    # per expert
+    "fp8_odd": WL["dsv3_fp8"].with_(name="fp8_odd", num_experts=16, top_k=4, d_model=512, d_ff=2304,
+                                    d_ff_shared=2304, n_group=4, topk_group=2),
 }
 
 
@@ -140,7 +150,8 @@ SMALL_LAYER = [("tiny", 16), ("tiny", 1), ("tiny", 17), ("tiny", 129), ("qwen3",
                ("qwen3", 32), ("qwen3", 128), ("qwen3", 3), ("k1_groups", 33), ("softmax_sel", 50),
                ("fp8_small", 1), ("fp8_small", 37), ("f32_shared", 40), ("tiled_small", 300),
                ("tiled_small", 129), ("tiled_narrow", 257), ("qwen3", 512),
-               ("fp8_rows", 200), ("fp8_rows", 67), ("cosched", 1), ("cosched", 45)]
+               ("fp8_rows", 200), ("fp8_rows", 67), ("cosched", 1), ("cosched", 45),
+               ("share_odd", 40), ("fp8_odd", 3), ("fp8_odd", 40)]
 
 
 @pytest.mark.parametrize("name,T", SMALL_LAYER)

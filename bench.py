@@ -278,6 +278,30 @@ def measure(layer, b, steps, warmup, flush, graph=False):
     return layer_us, ph, wall
 
 
+def measure_router(layer, b, wl, steps, flush):
+    """Mean µs of the router GEMM (moe_router_logits: logits = x W_r^T, fp32
+    out) for the batch's tokens, caches flushed before every call.  Reported
+    beside the layer, not inside it: the layer's input is the logits."""
+    import torch
+    import moe_inputs as mi
+    import combine_experts_amd as M
+    if wl.num_experts % 64:
+        return None
+    if getattr(layer, "w_router", None) is None:
+        wr = mi.gen_router_weight(wl)
+        layer.w_router = torch.from_numpy(wr.view(np.int16) if wr.dtype == np.uint16 else wr).cuda()
+    out = torch.empty((b.T, wl.num_experts), dtype=torch.float32, device="cuda")
+    M.moe_router_logits(layer.cfg, b.T, b.x, layer.w_router, out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s_, e_ in ev:
+        flush()
+        s_.record()
+        M.moe_router_logits(layer.cfg, b.T, b.x, layer.w_router, out)
+        e_.record()
+    torch.cuda.synchronize()
+    return float(np.mean([s_.elapsed_time(e_) * 1e3 for s_, e_ in ev]))
+
+
 def cpu_baseline(wl, T, seed=0):
     """The oracle, as it stands, on the headline workload: the whole layer
     for T tokens, all weights read from the generator's bf16 values."""
@@ -423,9 +447,16 @@ def main():
                                                         / counts.reshape(8, -1).sum(1).mean()), 3)
                 if wl.num_experts % 8 == 0 else None,
             }
+            rg_us = measure_router(layer, b, b_wl, args.steps, flush)
+            if rg_us is not None:
+                ab = _EB[b_wl.act_dtype]
+                rg_bytes = b_wl.num_experts * b_wl.d_model * ab + T * b_wl.d_model * ab + T * b_wl.num_experts * 4
+                ent["router_gemm_us"] = round(rg_us, 2)
+                ent["router_gemm_GBps"] = round(rg_bytes / rg_us / 1e3, 1)
             sweep.append(ent)
             log(f"[bench] {name} T={T}: layer {med:.1f} us (HBM {ent['hbm_frac'] * 100:.1f}% of peak, "
-                f"roof {ent['hbm_roof_us']:.1f} us), phases {ent['phase_us_mean']}")
+                f"roof {ent['hbm_roof_us']:.1f} us), phases {ent['phase_us_mean']}"
+                + (f", router GEMM {ent['router_gemm_us']} us" if "router_gemm_us" in ent else ""))
             if (name, T) == HEADLINE:
                 headline = (ent, layer_us, wall, gu_bytes, gu_flops, gu_us, b_wl)
             del b

@@ -74,8 +74,9 @@ def load_library():
     lib.moe_ffn_down.argtypes = [cp, i32, vp, wp, vp, sz, vp, vp, vp]
     lib.moe_combine.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_layer.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, sz, vp]
-    for f in (lib.moe_route, lib.moe_dispatch, lib.moe_route_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up, lib.moe_ffn_down,
-              lib.moe_combine, lib.moe_layer):
+    lib.moe_router_logits.argtypes = [cp, i32, vp, vp, vp, vp]
+    for f in (lib.moe_route, lib.moe_dispatch, lib.moe_route_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up,
+              lib.moe_ffn_down, lib.moe_combine, lib.moe_layer, lib.moe_router_logits):
         f.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -181,3 +182,8 @@ def moe_combine(cfg, T, expert_out, row_of, topk_w, shared_out, y, expert_count,
 def moe_layer(cfg, T, x, logits, bias, weights: MoeWeights, y, ws, ws_bytes, stream=None):
     _check(load_library().moe_layer(ctypes.byref(cfg), T, _ptr(x), _ptr(logits), _ptr(bias),
                                     ctypes.byref(weights), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_router_logits(cfg, T, x, w_router, logits, stream=None):
+    _check(load_library().moe_router_logits(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logits),
+                                            _stream(stream)))

@@ -738,6 +738,29 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
   return launch_plan<MOE_FP8_E4M3, false, MOE_F32>(q, pl, items, stream);
 }
 
+// The router GEMM at decode: its weight is small (E x d), so an item is one
+// 16-column tile (NM = 1) and the reduction is split eight ways inside the
+// workgroup, which spreads it over E / 16 workgroups of eight waves.
+template <int DT>
+static hipError_t launch_router_dt(const FfnParams& q, long long items, int steps, hipStream_t stream) {
+  if (steps >= 8) return launch_one<DT, 1, 8, 1, false, MOE_F32, 1>(q, items, stream);
+  if (steps >= 4) return launch_one<DT, 1, 4, 1, false, MOE_F32, 1>(q, items, stream);
+  return launch_one<DT, 1, 1, 1, false, MOE_F32, 1>(q, items, stream);
+}
+
+hipError_t launch_router_gemm(const FfnParams& p, int dtype, hipStream_t stream) {
+  const int step = dtype == MOE_F32 ? 64 : 128;
+  if (p.E != 0 || !p.masked || p.n_shared != 1 || p.Nout_s % 16 || p.K_s % step) return hipErrorInvalidValue;
+  FfnParams q = p;
+  q.tiles_r = 0;
+  q.tiles_s = p.Nout_s / 16;
+  const long long items = (long long)(p.T + 15) / 16 * q.tiles_s;
+  const int steps = p.K_s / step;
+  if (dtype == MOE_F32) return launch_router_dt<MOE_F32>(q, items, steps, stream);
+  if (dtype == MOE_BF16) return launch_router_dt<MOE_BF16>(q, items, steps, stream);
+  return hipErrorInvalidValue;
+}
+
 // ---------------------------------------------------------------------------
 // The router next to the shared expert's gate/up pass, in one launch
 // ("Hot-Expert Skew" section, shared experts; the shared expert needs no

@@ -376,6 +376,35 @@ moe_status moe_ffn_down(const moe_config* cfg, int32_t T, const int32_t* expert_
   return down_impl(cfg, T, expert_offset, w, ws, expert_out, shared_out, (hipStream_t)stream);
 }
 
+// The router GEMM is a plain pass over one group that holds all T tokens (the
+// slot the shared expert uses), with no routed groups and fp32 output: the
+// weight-streaming kernel at decode sizes, the LDS-tiled kernel (each weight
+// tile reused across 128 tokens) for 256 or more bf16 tokens.
+moe_status moe_router_logits(const moe_config* cfg, int32_t T, const void* x, const void* w_router,
+                             float* logits, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (cfg->num_experts % 64) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits || !all_aligned(x, w_router, logits)) return MOE_ERR_INVALID_ARG;
+  const int E = cfg->num_experts, d = cfg->d_model;
+  FfnParams r{};
+  r.E = 0;       // no routed groups
+  r.masked = 1;  // so no offsets array is read
+  r.T = T;
+  r.n_shared = 1;
+  r.tiles_r = 0;
+  r.tiles_s = E / 16;
+  r.K_r = d; r.NW_r = E; r.Nout_r = E;
+  r.s_act = static_cast<const uint8_t*>(x);
+  r.s_w = static_cast<const uint8_t*>(w_router);
+  r.K_s = d; r.NW_s = E; r.Nout_s = E;
+  r.s_out = logits;
+  if (cfg->act_dtype == MOE_BF16 && T >= 256 && E % 128 == 0) return hip_status(launch_gemm_tiled(r, false, 0, (hipStream_t)stream));
+  return hip_status(launch_router_gemm(r, cfg->act_dtype, (hipStream_t)stream));
+}
+
 moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out, const int32_t* row_of,
                        const float* topk_w, const float* shared_out, void* y, int32_t* expert_count,
                        void* stream) {

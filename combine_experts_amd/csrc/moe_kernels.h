@@ -98,6 +98,10 @@ hipError_t launch_route_shared(const RouteParams& rp, const FfnParams& sp, int w
 // max_token_tiles bounds the 128-row token tiles over the routed groups
 // (sizes the persistent grid).  Needs K % 64 == 0 and Nout % 128 == 0.
 hipError_t launch_gemm_tiled(const FfnParams& p, bool gated, long long max_token_tiles, hipStream_t stream);
+// Router GEMM over one group holding all T tokens (the shared-expert slot),
+// plain pass, fp32 out: one 16-column tile per item, K split KS ways inside
+// the workgroup, so a small router weight still spreads over E/16 workgroups.
+hipError_t launch_router_gemm(const FfnParams& p, int dtype, hipStream_t stream);
 
 // FfnParams::tiles_r / tiles_s count 16-column tiles; launch_ffn groups them
 // into the work items of the launch shape it picks (a gated E4M3 pass always

@@ -260,6 +260,24 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
                        int32_t* expert_count, void* stream);
 
 /*
+ * moe_router_logits: the router's scores before the score function,
+ * logits[t][e] = sum_c x[t][c] * w_router[e][c], accumulated in fp32
+ * ("7.13 Serving Mixture-of-Experts", moe_ep_layer listing: the router is a
+ * linear map of the token to one score per expert, followed by the softmax
+ * and top-k that moe_route applies).  Its output is moe_route's (and
+ * moe_layer's) logits input.
+ *   x        [T][d] act_dtype (bf16 for the bf16 and E4M3 layers, fp32 for
+ *            the fp32 layer), K-contiguous.
+ *   w_router [E][d] act_dtype, K-contiguous (one row per expert).
+ *   logits   [T][E] fp32, written.
+ * The products are exact in fp32 and are summed in fp32 in a fixed order, so
+ * the result is reproducible run to run.  Requires E % 64 == 0
+ * (MOE_ERR_UNSUPPORTED otherwise).  Needs no workspace.
+ */
+moe_status moe_router_logits(const moe_config* cfg, int32_t T, const void* x, const void* w_router,
+                             float* logits, void* stream);
+
+/*
  * moe_layer: route -> dispatch -> expert FFN (+ shared expert) -> combine in
  * one call, every intermediate carved from ws (>= moe_workspace_size(cfg, T)
  * bytes, zero-filled once by the caller).  Launches only; no host sync, so

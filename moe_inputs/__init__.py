@@ -27,6 +27,7 @@ _lock = threading.Lock()
 
 # Tensor ids of the counter streams.
 TID_X, TID_LOGITS, TID_BIAS, TID_W13, TID_W2, TID_WS13, TID_WS2, TID_PERM = 1, 2, 3, 4, 5, 6, 7, 8
+TID_WR = 9
 
 
 def build_lib(force: bool = False) -> str:
@@ -166,6 +167,17 @@ def gen_x(w: Workload, T: int, seed: int = 0) -> np.ndarray:
 def gen_logits(w: Workload, T: int, seed: int = 0) -> np.ndarray:
     """Router logits [T][E] fp32, N(0, 1)."""
     return normal_f32(seed, TID_LOGITS, (T, w.num_experts), 1.0)
+
+
+def gen_router_weight(w: Workload, seed: int = 0) -> np.ndarray:
+    """Router weight [E][d] in the activation dtype, N(0, 1/d): with N(0, 1)
+    tokens the router logits come out about N(0, 1), the logit distribution
+    of the decode workloads."""
+    shape = (w.num_experts, w.d_model)
+    std = float(1.0 / np.sqrt(w.d_model))
+    if w.act_dtype == "f32":
+        return normal_f32(seed, TID_WR, shape, std)
+    return normal_bf16(seed, TID_WR, shape, std)
 
 
 def gen_bias(w: Workload, seed: int = 0):

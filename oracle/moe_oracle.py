@@ -19,6 +19,10 @@ Sources (page title, then section):
   [P4]  "Mixture-of-experts serving" (learn-kernels), paragraphs 1 and 4.
 
 What is pinned, and how (tests/test_oracle_pins.py):
+  router logits    one-hot tokens select one weight column; zero tokens give
+                   zero logits; identity router weights give the token back;
+                   with them, routing from the hidden state picks the token's
+                   largest coordinates.
   route            brute-force enumeration on small E; invariants; the
                    expected-distinct-experts closed form of [P2] "Why MoE
                    Serving..." (Monte Carlo); softmax identity.
@@ -126,6 +130,15 @@ def choose_groups(gscores, topk_group):
     chosen = np.zeros((T, G), dtype=bool)
     np.put_along_axis(chosen, order[:, :topk_group], True, axis=1)
     return chosen
+
+
+def router_logits(x, w_router):
+    """Router scores before the score function: logits[t][e] = x[t] . w_router[e].
+
+    [P2] moe_ep_layer listing: the router is one linear map from the token to
+    a score per expert; softmax and top-k (route below) follow.  Float64
+    matrix product of the stored values."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w_router, dtype=np.float64).T
 
 
 def route(logits, bias, spec):

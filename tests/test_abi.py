@@ -145,3 +145,20 @@ def test_masked_layout_sizes_and_argument_checks(M):
     with pytest.raises(M.MoeError) as e:
         M.moe_dispatch(dsv3(M), 4, 16, 16, 16, 16, 16, None, None, 16, stream=0)
     assert e.value.status == M.MOE_ERR_INVALID_ARG
+
+
+def test_router_logits_argument_checks(M):
+    cfg = dsv3(M)
+    M.moe_router_logits(cfg, 0, None, None, None, stream=0)  # T = 0: nothing to do
+    with pytest.raises(M.MoeError) as e:
+        M.moe_router_logits(cfg, 4, None, 16, 16, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_router_logits(cfg, 4, 16, 24, 16, stream=0)  # misaligned router weight
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_router_logits(cfg, -1, 16, 16, 16, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:  # E not a multiple of 64
+        M.moe_router_logits(dsv3(M, num_experts=96, n_group=8, topk_group=4), 4, 16, 16, 16, stream=0)
+    assert e.value.status == M.MOE_ERR_UNSUPPORTED

@@ -1,0 +1,78 @@
+"""The router's logits x W_r^T on the GPU, through the C ABI ("7.13 Serving
+Mixture-of-Experts", moe_ep_layer listing: the router is a linear map from
+the token to one score per expert, then softmax and top-k).
+
+The GPU forms the products (exact for bf16 x bf16) and sums them in fp32, in
+an order of its own.  For any order, the error of K products summed with a
+rounding at each product and each addition is at most gamma_{K+1} * sum_c
+|x_c w_c|, gamma_n = n u / (1 - n u); u = 2^-23 covers both rounding to
+nearest and truncation.  Every logit must lie within that bound of the
+oracle's float64 product.  Routing from those logits may then differ from routing on
+the exact logits only for tokens whose deciding keys (k-th against (k+1)-th
+expert, or the group boundary) are closer than the keys can move."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from moe_case import TIE, cfg_of, dev, host, say, x_values
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+WL = mi.WORKLOADS
+CASES = {
+    "qwen3": WL["qwen3"],
+    "dsv3": WL["dsv3"],
+    "dsv3_prefill": WL["dsv3_prefill"],
+    # the fp32 layer's widths with 64 experts (the router GEMM needs E % 64 == 0)
+    "f32_64": WL["tiny"].with_(name="f32_64", num_experts=64, top_k=4, x_std=1.0),
+    # bf16, 64 experts: many tokens still take the streaming kernel (the tiled
+    # one needs E % 128 == 0)
+    "bf16_64": WL["qwen3"].with_(name="bf16_64", num_experts=64, top_k=4),
+}
+
+
+def fp32_sum_bound(xv, wv):
+    n = xv.shape[1] + 1
+    u = 2.0 ** -23
+    return (n * u / (1.0 - n * u)) * (np.abs(xv) @ np.abs(wv).T)
+
+
+@pytest.mark.parametrize("name,T", [("qwen3", 1), ("qwen3", 37), ("qwen3", 128), ("qwen3", 512), ("dsv3", 1),
+                                    ("dsv3", 8), ("dsv3", 128), ("dsv3_prefill", 4096), ("f32_64", 16),
+                                    ("f32_64", 129), ("bf16_64", 300), ("dsv3", 300)])
+def test_router_logits(name, T):
+    import combine_experts_amd as M
+    say(f"\n[gpu-test] router logits {name} T={T}")
+    wl = CASES[name]
+    E = wl.num_experts
+    x = mi.gen_x(wl, T)
+    wr = mi.gen_router_weight(wl)
+    xd, wd = dev(x), dev(wr)
+    out = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    M.moe_router_logits(cfg_of(wl), T, xd, wd, out)
+    again = torch.full_like(out, float("nan"))
+    M.moe_router_logits(cfg_of(wl), T, xd, wd, again)
+    torch.cuda.synchronize()
+    got = host(out).astype(np.float64)
+    assert np.array_equal(host(out).view(np.uint32), host(again).view(np.uint32)), "not reproducible"
+    xv, wv = x_values(wl, x), x_values(wl, wr)
+    ref = O.router_logits(xv, wv)
+    bound = fp32_sum_bound(xv, wv)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), float((err / bound).max())
+    # routing from the GPU's logits against routing from the exact ones
+    bias = mi.gen_bias(wl)
+    idx_gpu, _, _ = O.route(host(out), bias, wl)
+    idx_ref, _, info = O.route(ref.astype(np.float32), bias, wl)
+    moved = bound.max(axis=1) + np.abs(ref).max(axis=1) * 2.0 ** -24  # fp32 rounding of the logit too
+    # keys move at most as much as the logits (the sigmoid's slope is at most
+    # 1/4); a group score is a sum of two keys
+    slack = 4.0 * moved + TIE
+    differ = (np.sort(idx_gpu, axis=1) != np.sort(idx_ref, axis=1)).any(axis=1)
+    margin = O.routing_margins(info, wl)
+    assert not (differ & ~(margin <= slack)).any()
+    say(f"  max |err| / bound = {float((err / bound).max()):.3f}, max |err| = {float(err.max()):.2e}, "
+        f"{int(differ.sum())} of {T} tokens route differently (all near ties)")

@@ -416,3 +416,37 @@ def test_fp8_path_dispatch_equals_dense_and_stays_close():
                            rtol=1e-12, atol=1e-12)
     rel = np.abs(yq - y).max() / np.abs(y).max()
     assert 0 < rel < 0.1
+
+
+# ---------------------------------------------------------------------------
+# router logits ([P2] moe_ep_layer listing: a linear map, then softmax/top-k)
+# ---------------------------------------------------------------------------
+
+
+def test_router_logits_special_cases():
+    rng = np.random.default_rng(5)
+    E, d = 6, 10
+    wr = rng.standard_normal((E, d))
+    # a one-hot token picks one column of the router weight, exactly
+    for c in range(d):
+        x = np.zeros((1, d))
+        x[0, c] = 1.0
+        assert np.array_equal(O.router_logits(x, wr)[0], wr[:, c])
+    # zero tokens score zero
+    assert np.array_equal(O.router_logits(np.zeros((3, d)), wr), np.zeros((3, E)))
+    # identity router weights (E = d) hand the token back
+    x = rng.standard_normal((4, d))
+    assert np.array_equal(O.router_logits(x, np.eye(d)), x)
+
+
+def test_route_from_hidden_state_with_identity_router():
+    # with identity router weights, softmax routing from the hidden state takes
+    # each token's k largest coordinates, in descending order
+    rng = np.random.default_rng(6)
+    spec = mi.WORKLOADS["qwen3"].with_(num_experts=16, top_k=3, d_model=16)
+    x = rng.permuted(np.tile(np.arange(16, dtype=np.float64), (5, 1)), axis=1)
+    logits = O.router_logits(x, np.eye(16)).astype(np.float32)
+    idx, w, _ = O.route(logits, None, spec)
+    for t in range(5):
+        assert list(idx[t]) == list(np.argsort(-x[t], kind="stable")[:3])
+        assert abs(w[t].sum() - 1.0) < 1e-12

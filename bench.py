@@ -361,6 +361,9 @@ def main():
     ap.add_argument("--tokens", default=None, help="override the token counts, e.g. 1,8,128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between steps")
+    ap.add_argument("--no-router", action="store_true",
+                    help="skip timing the router GEMM (its prefill-sized launches use the same tiled kernel "
+                         "as the down pass, which would mix the two in a profile)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of moe_layer captured in a HIP graph instead of direct calls")
     ap.add_argument("--layout", choices=("compact", "masked"), default="compact",
@@ -447,7 +450,7 @@ def main():
                                                         / counts.reshape(8, -1).sum(1).mean()), 3)
                 if wl.num_experts % 8 == 0 else None,
             }
-            rg_us = measure_router(layer, b, b_wl, args.steps, flush)
+            rg_us = None if args.no_router else measure_router(layer, b, b_wl, args.steps, flush)
             if rg_us is not None:
                 ab = _EB[b_wl.act_dtype]
                 rg_bytes = b_wl.num_experts * b_wl.d_model * ab + T * b_wl.d_model * ab + T * b_wl.num_experts * 4

@@ -595,28 +595,31 @@ static constexpr int kResidentCap = MOE_FFN_RESIDENT;
 template <int DT, int FW, int KS, int TT, bool GATED, int OUT, int NM = 2, bool PARK = true, bool SHARE = false>
 static hipError_t launch_one(const FfnParams& p, long long max_items, hipStream_t stream) {
   auto kern = ffn_kernel<DT, FW, KS, TT, GATED, OUT, NM, PARK, SHARE>;
-  // constant per kernel and device model
-  static int per_cu = -1, cus = -1;
-  static size_t reserve = 0;
-  if (per_cu < 0) {
+  // constant per kernel and device model: computed once, on the first call
+  // (thread-safe initialisation of a const local static)
+  static const Residency occ = [&] {
+    Residency o{};
     int dev = 0, n = 0, c = 0, lds = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipGetDevice(&dev) != hipSuccess) return o;
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 256;
     if (DT != MOE_FP8_E4M3 && kResidentCap > 0 &&
         hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) == hipSuccess &&
         lds > 0) {
       const size_t r = (size_t)lds / (kResidentCap + 1) + 1;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * FW * KS, r) == hipSuccess && n >= 1)
-        reserve = r;
+        o.reserve = r;
     }
-    if (reserve == 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * FW * KS, 0) != hipSuccess)
+    if (o.reserve == 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 64 * FW * KS, 0) != hipSuccess)
       n = 1;
-    cus = c;
-    per_cu = n > 0 ? n : 1;
-  }
-  const long long cap = (long long)per_cu * cus;
+    o.cus = c;
+    o.per_cu = n > 0 ? n : 1;
+    o.ok = true;
+    return o;
+  }();
+  if (!occ.ok) return hipErrorInvalidDevice;
+  const long long cap = (long long)occ.per_cu * occ.cus;
   const int grid = (int)(max_items < cap ? max_items : cap);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * FW * KS), reserve, stream, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * FW * KS), occ.reserve, stream, p);
   return hipGetLastError();
 }
 
@@ -788,18 +791,21 @@ static hipError_t launch_rs(const RouteParams& rp, const FfnParams& q, long long
   constexpr int NT = 64 * FW * KS;
   const size_t lds = (size_t)(FW * KS) * route_lds_floats(rp.E) * sizeof(float);
   // workgroups per CU for the largest routing LDS (E = 1024), constant per
-  // kernel and device model
-  static int per_cu = -1, cus = -1;
-  if (per_cu < 0) {
+  // kernel and device model: computed once (thread-safe static initialisation)
+  static const Residency occ = [&] {
+    Residency o{};
     int dev = 0, n = 0, c = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipGetDevice(&dev) != hipSuccess) return o;
     const size_t lds_max = (size_t)(FW * KS) * route_lds_floats(1024) * sizeof(float);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, NT, lds_max) != hipSuccess || n < 1) n = 1;
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 256;
-    per_cu = n;
-    cus = c;
-  }
-  const long long cap = (long long)per_cu * cus;
+    o.per_cu = n;
+    o.cus = c;
+    o.ok = true;
+    return o;
+  }();
+  if (!occ.ok) return hipErrorInvalidDevice;
+  const long long cap = (long long)occ.per_cu * occ.cus;
   const int nroute = rp.fuse ? rp.T : (rp.T + FW * KS - 1) / (FW * KS);
   const int nshared = (int)(items < cap ? items : cap);
   hipLaunchKernelGGL(kern, dim3(nroute + nshared), dim3(NT), lds, stream, rp, q, nroute);

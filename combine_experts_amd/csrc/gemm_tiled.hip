@@ -339,16 +339,21 @@ static hipError_t launch_wr(const FfnParams& p, long long max_token_tiles, hipSt
   const long long max_items = max_token_tiles * (p.Nout_r / fcols) +
                               (p.n_shared ? (long long)((p.T + BN - 1) / BN) * (p.Nout_s / fcols) : 0);
   auto kern = gemm_tiled_kernel<GATED, WR>;
-  static int per_cu = -1, cus = -1;  // constant per kernel and device model
-  if (per_cu < 0) {
+  // constant per kernel and device model: computed once (thread-safe
+  // initialisation of a const local static)
+  static const Residency occ = [&] {
+    Residency o{};
     int dev = 0, n = 0, c = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipGetDevice(&dev) != hipSuccess) return o;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, 2 * WR, 0) != hipSuccess) n = 1;
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 256;
-    per_cu = n > 0 ? n : 1;
-    cus = c;
-  }
-  const long long cap = (long long)per_cu * cus;
+    o.per_cu = n > 0 ? n : 1;
+    o.cus = c;
+    o.ok = true;
+    return o;
+  }();
+  if (!occ.ok) return hipErrorInvalidDevice;
+  const long long cap = (long long)occ.per_cu * occ.cus;
   const int grid = (int)(max_items < cap ? max_items : cap);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(2 * WR), 0, stream, p);

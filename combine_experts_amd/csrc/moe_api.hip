@@ -376,9 +376,10 @@ moe_status moe_ffn_down(const moe_config* cfg, int32_t T, const int32_t* expert_
   return down_impl(cfg, T, expert_offset, w, ws, expert_out, shared_out, (hipStream_t)stream);
 }
 
-// The router GEMM is a plain pass over one group that holds all T tokens (the
-// slot the shared expert uses), with no routed groups and fp32 output: the
-// weight-streaming kernel up to 2047 tokens, the LDS-tiled kernel (each
+// The router GEMM: dot products for up to 16 tokens (one workgroup per
+// expert); above that a plain pass over one group that holds all T tokens
+// (the slot the shared expert uses), with no routed groups and fp32 output:
+// the weight-streaming kernel up to 2047 tokens, the LDS-tiled kernel (each
 // weight tile reused across 128 tokens) from 2048 bf16 tokens on.  The tiled
 // kernel has only T/128 x E/256 items here, so below that it leaves most CUs
 // idle (512 tokens: 111 us tiled).
@@ -403,6 +404,8 @@ moe_status moe_router_logits(const moe_config* cfg, int32_t T, const void* x, co
   r.s_w = static_cast<const uint8_t*>(w_router);
   r.K_s = d; r.NW_s = E; r.Nout_s = E;
   r.s_out = logits;
+  if (router_gemv_fits(T, d, cfg->act_dtype))
+    return hip_status(launch_router_gemv(x, w_router, logits, T, E, d, cfg->act_dtype, (hipStream_t)stream));
   if (cfg->act_dtype == MOE_BF16 && T >= 2048 && E % 128 == 0) return hip_status(launch_gemm_tiled(r, false, 0, (hipStream_t)stream));
   return hip_status(launch_router_gemm(r, cfg->act_dtype, (hipStream_t)stream));
 }

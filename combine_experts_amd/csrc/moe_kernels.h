@@ -97,11 +97,26 @@ hipError_t launch_route_shared(const RouteParams& rp, const FfnParams& sp, int w
 // LDS-tiled bf16 grouped GEMM for groups with many rows (prefill);
 // max_token_tiles bounds the 128-row token tiles over the routed groups
 // (sizes the persistent grid).  Needs K % 64 == 0 and Nout % 128 == 0.
+// Resident workgroups of one kernel: per CU, CU count, and the dynamic LDS
+// reserved to cap residency.  Launchers compute it once per kernel, on first
+// use, into a const local static.
+struct Residency {
+  int per_cu = 1, cus = 0;
+  size_t reserve = 0;
+  bool ok = false;
+};
+
 hipError_t launch_gemm_tiled(const FfnParams& p, bool gated, long long max_token_tiles, hipStream_t stream);
 // Router GEMM over one group holding all T tokens (the shared-expert slot),
 // plain pass, fp32 out: one 16-column tile per item, K split KS ways inside
 // the workgroup, so a small router weight still spreads over E/16 workgroups.
 hipError_t launch_router_gemm(const FfnParams& p, int dtype, hipStream_t stream);
+// Router GEMM for 1-16 tokens as dot products: one workgroup per expert, the
+// reduction split over its four waves.  router_gemv_fits says whether the
+// shape is covered (d up to 16384 bf16 / 8192 fp32).
+bool router_gemv_fits(int T, int d, int dtype);
+hipError_t launch_router_gemv(const void* x, const void* w, float* logits, int T, int E, int d, int dtype,
+                              hipStream_t stream);
 
 // FfnParams::tiles_r / tiles_s count 16-column tiles; launch_ffn groups them
 // into the work items of the launch shape it picks (a gated E4M3 pass always

@@ -690,6 +690,19 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
         break;
       }
   }
+  // A bf16 plain pass with short items (under 16 steps) and eight or more
+  // rows per touched expert: four column waves sharing each activation tile.
+  // Measured at 128 experts x 8 slots, d_ff = 768 (6 steps), down pass with
+  // (2, 1) private / (4, 1) shared tiles, two runs each: 128 tokens
+  // 80.7, 81.3 / 78.7, 78.5 us; 256 tokens 108.5, 109.3 / 99.5, 100.0 us.
+  // With fewer rows per expert the tiles are mostly padding and sharing them
+  // does not pay (32 tokens: 67.7 against 71.6 us).
+  const bool dense_plain = !gated && wdtype == MOE_BF16 && routed_rows >= 8LL * max_groups;
+  if (dense_plain) {
+    int st = p.K_r / step;
+    if (p.n_shared && p.K_s / step < st) st = p.K_s / step;
+    if (st < 16 && p.tiles_r % 8 == 0 && p.tiles_s % 8 == 0) pl = Plan{4, 1};
+  }
 #endif
   // a work item covers FW waves' columns; a plain-pass wave covers two tiles
   const int per_item = pl.fw * (gated ? 1 : 2);
@@ -711,13 +724,19 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
   // every wave of a workgroup walks the same number of steps per item
   const bool even = (q.K_r / step) % pl.ks == 0 && (!q.n_shared || (q.K_s / step) % pl.ks == 0);
   if (wdtype == MOE_BF16) {
-    // bf16 tiles are shared only between column waves of items with 16 or
-    // more steps: measured at 128 tokens, 128 experts: gate/up (16 steps)
-    // 143.0 -> 141.5 us, but the 6-step down pass 80.4 -> 84.2 us; 256
-    // experts: down (16 steps) 941 -> 916 us
+    // bf16 tiles are shared between column waves of items with 16 or more
+    // steps: measured at 128 tokens, 128 experts: gate/up (16 steps) 143.0 ->
+    // 141.5 us, but the 6-step down pass with (2, 1) 80.4 -> 84.2 us; 256
+    // experts: down (16 steps) 941 -> 916 us.  Short dense plain passes share
+    // under the (4, 1) shape chosen above.
     int steps = q.K_r / step;
     if (q.n_shared && q.K_s / step < steps) steps = q.K_s / step;
-    if (pl.fw >= 2 && steps >= 16 && even) {
+#ifndef MOE_FFN_FW
+    const bool dense4 = dense_plain && pl.fw == 4 && pl.ks == 1;
+#else
+    const bool dense4 = false;
+#endif
+    if ((pl.fw >= 2 && steps >= 16 && even) || dense4) {
       if (gated) return launch_plan<MOE_BF16, true, MOE_BF16, 1, true, true>(q, pl, items, stream);
       return launch_plan<MOE_BF16, false, MOE_F32, 1, true, true>(q, pl, items, stream);
     }

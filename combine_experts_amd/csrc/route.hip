@@ -17,16 +17,60 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams p) {
   route_body<KPL, 4>(p, blockIdx.x, smem);
 }
 
+// Large batches: 16 tokens per workgroup, and the tickets of the workgroup's
+// slots reserved with one atomic per expert.  Each slot first takes its rank
+// among the workgroup's slots of its expert (an LDS atomic); then one thread
+// per expert adds the workgroup's count to the expert's counter and gets the
+// base.  A hot expert's counter then sees one atomic per workgroup instead of
+// one per slot (4096 tokens with Zipf-skewed routing: up to 2119 slots of one
+// expert).  Which ticket a slot gets within its expert is not fixed either
+// way; the set of tickets is 0 .. count - 1.
+constexpr int kAggWaves = 16;
+
+template <int KPL>
+__global__ __launch_bounds__(64 * kAggWaves) void route_agg_kernel(RouteParams p) {
+  extern __shared__ float smem[];
+  __shared__ int cnt[256], base[256];
+  for (int e = threadIdx.x; e < p.E; e += 64 * kAggWaves) cnt[e] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kAggWaves + (threadIdx.x >> 6);
+  const int e = route_body<KPL, kAggWaves, false>(p, blockIdx.x, smem);
+  const bool slot = t < p.T && lane < p.k;
+  int rank = 0;
+  if (slot) rank = atomicAdd(&cnt[e], 1);
+  __syncthreads();
+  for (int g = threadIdx.x; g < p.E; g += 64 * kAggWaves)
+    if (cnt[g] > 0) base[g] = atomicAdd(p.expert_count + g, cnt[g]);
+  __syncthreads();
+  if (slot) p.ticket[(size_t)t * p.k + lane] = base[e] + rank;
+}
+
 template <int KPL>
 __global__ __launch_bounds__(256) void route_dispatch_kernel(RouteParams p) {
   extern __shared__ float smem[];
   route_dispatch_block<KPL>(p, blockIdx.x, smem);
 }
 
-// Four tokens per workgroup, one per wave; with the masked-layout write
-// (p.fuse) one token per workgroup, whose four waves share the copy.
+// Four tokens per workgroup, one per wave (256 tokens or more: sixteen, with
+// tickets reserved per workgroup); with the masked-layout write (p.fuse) one
+// token per workgroup, whose four waves share the copy.
 hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
   const int kpl_needed = (p.E + 63) / 64;
+  if (!p.fuse && p.T >= 256 && p.E <= 256 && p.ticket) {  // LDS: 16 waves x (2E + 384) floats <= 57 KB
+    const int blocks = (p.T + kAggWaves - 1) / kAggWaves;
+    const size_t lds = kAggWaves * (size_t)route_lds_floats(p.E) * sizeof(float);
+#define MOE_AGG_CASE(K)                                                                                 \
+    if (kpl_needed <= K) {                                                                              \
+      hipLaunchKernelGGL(route_agg_kernel<K>, dim3(blocks), dim3(64 * kAggWaves), lds, stream, p);     \
+      return hipGetLastError();                                                                         \
+    }
+    MOE_AGG_CASE(1)
+    MOE_AGG_CASE(2)
+    MOE_AGG_CASE(4)
+    MOE_AGG_CASE(8)
+#undef MOE_AGG_CASE
+  }
   const int nw = p.fuse ? 1 : 4;
   const int blocks = (p.T + nw - 1) / nw;
   const size_t lds = nw * (size_t)route_lds_floats(p.E) * sizeof(float);

@@ -34,8 +34,10 @@ __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m)
 // Routes token bid * NW + w with wave w of an NW-wave block; smem holds
 // route_lds_floats(E) floats per wave.  Returns, in lane j < k, the
 // masked-layout row of the token's slot j (when p.fuse; 0 otherwise), and -1
-// in every lane when the token is past T.
-template <int KPL, int NW>
+// in every lane when the token is past T.  With TICKET = false the slots take
+// no ticket here (the caller reserves them) and lane j < k returns the
+// expert of slot j instead.
+template <int KPL, int NW, bool TICKET = true>
 __device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* smem) {
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -249,11 +251,15 @@ __device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* 
     const size_t o = (size_t)t * k + lane;
     p.topk_idx[o] = my_idx;
     p.topk_w[o] = w;
-    const int tk = atomicAdd(p.expert_count + my_idx, 1);
-    if (p.ticket) p.ticket[o] = tk;
-    if (p.fuse) {
-      my_row = my_idx * p.T + tk;
-      p.row_of[o] = my_row;
+    if constexpr (TICKET) {
+      const int tk = atomicAdd(p.expert_count + my_idx, 1);
+      if (p.ticket) p.ticket[o] = tk;
+      if (p.fuse) {
+        my_row = my_idx * p.T + tk;
+        p.row_of[o] = my_row;
+      }
+    } else {
+      my_row = my_idx;
     }
   }
   return my_row;

@@ -85,3 +85,63 @@ def test_graph_replays_match_eager(name, T, masked):
             # unrelated eager work between replays
             (torch.randn(1 << 16, device="cuda") * 2).sum().item()
     say(f"  {name} T={T}: 6 replays equal the eager calls")
+
+
+@pytest.mark.parametrize("T", [8, 40])
+def test_graph_router_gemm_then_layer(T):
+    """moe_router_logits then moe_layer, from hidden states, in one capture:
+    every replay equals the eager pair on the same tokens (T = 8 takes the
+    dot-product router kernel, T = 40 the streaming one)."""
+    import combine_experts_amd as M
+    from moe_case import dev
+    say(f"\n[gpu-test] graph router GEMM + layer T={T}")
+    wl = WL["dsv3"].with_(name="router_graph", num_experts=64, top_k=4, d_model=1024, d_ff=256,
+                          d_ff_shared=512, n_group=4, topk_group=2)
+    cfg = cfg_of(wl)
+    wr = dev(mi.gen_router_weight(wl))
+    inps = [Inputs(wl, T, seed=s) for s in (21, 22, 23)]
+    ws_bytes = M.moe_workspace_size(cfg, T)
+    W = Weights(wl, experts=[])
+
+    def run(x, logits, y, ws):
+        M.moe_router_logits(cfg, T, x, wr, logits)
+        M.moe_layer(cfg, T, x, logits, inps[0].bias_d, W.moe_weights(), y, ws, ws_bytes)
+
+    # the experts the router picks, so that their weights are in place
+    for inp in inps:
+        lg = torch.empty((T, wl.num_experts), dtype=torch.float32, device="cuda")
+        M.moe_router_logits(cfg, T, inp.x, wr, lg)
+        torch.cuda.synchronize()
+        W.ensure(np.unique(O.route(host(lg), inps[0].bias, wl)[0]))  # the bias run() passes
+
+    def eager(inp):
+        lg = torch.empty((T, wl.num_experts), dtype=torch.float32, device="cuda")
+        y = torch.empty((T, wl.d_model), dtype=torch.int16, device="cuda")
+        run(inp.x, lg, y, torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        return host(y)
+
+    want = [eager(inp) for inp in inps]
+    for w in want:  # every expert the layer used holds real weights
+        assert np.isfinite(mi.bf16_bits_to_f32(w)).all()
+    x = inps[0].x.clone()
+    logits = torch.empty((T, wl.num_experts), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, wl.d_model), dtype=torch.int16, device="cuda")
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    run(x, logits, y, ws)  # launch-shape queries outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run(x, logits, y, ws)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, inp in enumerate(inps):
+            x.copy_(inp.x)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(host(y), want[i]), (rep, i)
+            (torch.randn(1 << 16, device="cuda") * 2).sum().item()
+    say(f"  router GEMM + layer T={T}: 6 replays equal the eager calls")

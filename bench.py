@@ -374,7 +374,7 @@ def main():
                          "scaling the profiler's byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (--gpus {args.gpus} "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (--gpus {args.gpus} "
               "requested). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

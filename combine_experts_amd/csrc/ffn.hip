@@ -690,6 +690,17 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
         break;
       }
   }
+  // A bf16 gated pass of 16-31 steps with under two rows per touched expert
+  // and at least 32 of them: one column wave per item and a 4-way K-split.
+  // Measured at 128 experts x 8 slots, d_model = 2048, (2, 2) against (1, 4),
+  // two runs each: 8 tokens 62.1, 62.3 / 58.7, 59.1 us.  It loses at 1 token
+  // (8 experts: 19.3, 19.5 / 20.8, 20.1 us) and from 32 tokens on (126.5,
+  // 126.3 / 131.4, 131.5 us; 128 tokens 141.9, 142.2 / 153.8, 153.9 us).
+  // Not with a shared expert, whose items moe_layer may run in the router's
+  // launch with the shape of plan_of.
+  if (gated && wdtype == MOE_BF16 && !p.n_shared && max_groups >= 32 && routed_rows < 2LL * max_groups &&
+      p.K_r / step >= 16 && p.K_r / step < 32)
+    pl = Plan{1, 4};
   // A bf16 plain pass with short items (under 16 steps) and eight or more
   // rows per touched expert: four column waves sharing each activation tile.
   // Measured at 128 experts x 8 slots, d_ff = 768 (6 steps), down pass with

@@ -366,8 +366,9 @@ def main():
                          "as the down pass, which would mix the two in a profile)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of moe_layer captured in a HIP graph instead of direct calls")
-    ap.add_argument("--layout", choices=("compact", "masked"), default="compact",
-                    help="dispatch layout: compact (T*k rows from a scan of the counters) or masked "
+    ap.add_argument("--layout", choices=("auto", "compact", "masked"), default="auto",
+                    help="dispatch layout: auto (masked for bf16 layers at 8 tokens or fewer, compact "
+                         "otherwise), compact (T*k rows from a scan of the counters) or masked "
                          "(E*T rows, route and dispatch in one launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB device-to-device 3 times (a plain copy of known size for "
@@ -416,6 +417,13 @@ def main():
         if args.tokens:
             toks = tuple(int(t) for t in args.tokens.split(","))
         for T in toks:
+            # auto: the masked layout (route and dispatch in one launch) where
+            # it measured faster, at bf16 decode of 8 tokens or fewer (Qwen3
+            # shapes 1 token 42.1 -> 38.2 us, 8 tokens 101.6 -> 98.3 us; at 128
+            # tokens compact is faster, 233 against 240 us)
+            if args.layout == "auto":
+                layer.masked = T <= 8 and wl.weight_dtype == "bf16"
+                layer.cfg.masked_layout = 1 if layer.masked else 0
             b = Batch(layer, wl, T)
             b_wl = wl
             D, counts = touched_experts(layer, b)
@@ -426,7 +434,7 @@ def main():
             gu_us = float(ph[:, 2].mean())
             peak_t = MFMA_PEAK_TFLOPS[b_wl.weight_dtype]
             ent = {
-                "workload": WORKLOAD_NAMES[name], "tokens": T, "layout": args.layout,
+                "workload": WORKLOAD_NAMES[name], "tokens": T, "layout": "masked" if layer.masked else "compact",
                 "launch": "hip graph replay" if args.graph else "direct", "touched_experts": D,
                 "layer_us_median": round(med, 2), "layer_us_p10": round(float(np.percentile(layer_us, 10)), 2),
                 "layer_us_p90": round(float(np.percentile(layer_us, 90)), 2),

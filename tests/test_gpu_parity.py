@@ -62,7 +62,7 @@ def wl_of(name):
 ROUTE_CASES = [("tiny", 16), ("tiny", 1), ("tiny", 129), ("qwen3", 1), ("qwen3", 8), ("qwen3", 32),
                ("qwen3", 128), ("qwen3", 3), ("dsv3", 1), ("dsv3", 8), ("dsv3", 32), ("dsv3", 128),
                ("dsv3", 17), ("dsv3_fp8", 512), ("dsv3_prefill", 4096), ("k1_groups", 33),
-               ("softmax_sel", 50)]
+               ("softmax_sel", 50), ("qwen3", 255), ("qwen3", 256), ("dsv3", 256), ("dsv3", 300)]
 
 
 @pytest.fixture(autouse=True)

@@ -41,7 +41,8 @@ def fp32_sum_bound(xv, wv):
 
 @pytest.mark.parametrize("name,T", [("qwen3", 1), ("qwen3", 37), ("qwen3", 128), ("qwen3", 512), ("dsv3", 1),
                                     ("dsv3", 8), ("dsv3", 128), ("dsv3_prefill", 4096), ("f32_64", 16),
-                                    ("f32_64", 129), ("bf16_64", 300), ("dsv3", 300), ("dsv3", 2048), ("qwen3", 2048)])
+                                    ("f32_64", 129), ("bf16_64", 300), ("dsv3", 300), ("dsv3", 2048), ("qwen3", 2048),
+                                    ("qwen3", 16), ("qwen3", 17), ("dsv3", 16), ("dsv3", 17)])
 def test_router_logits(name, T):
     import combine_experts_amd as M
     say(f"\n[gpu-test] router logits {name} T={T}")

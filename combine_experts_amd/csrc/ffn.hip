@@ -27,6 +27,14 @@
 //    Loads are never skipped (a stage past the end repeats the last address,
 //    a token row past a group's end reads the group's first row and its
 //    column is never stored), which keeps the wait counts exact.
+//  * A CU takes in only so many bytes per microsecond when its loads mix HBM
+//    misses with L2 hits, and every column wave needs the same activation
+//    tile at a step.  Where the waves of a workgroup walk the same steps,
+//    they share that tile through LDS (SHARE, below) instead of each loading
+//    it; the launch plan (launch_ffn) picks the shape per pass from the
+//    K-steps per item and the rows per touched expert.
+//  * The same walk, with one group holding all T tokens and fp32 output, is
+//    the router GEMM for 17-2047 tokens (launch_router_gemm).
 #include "route_body.h"
 
 namespace moe {

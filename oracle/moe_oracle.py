@@ -29,6 +29,7 @@ What is pinned, and how (tests/test_oracle_pins.py):
   dispatch/combine exact inverse permutation; counts = bincount.
   expert FFN       an independent dense per-token path; closed forms (x = 0,
                    zero up-projection, d = F = 1 by hand, E = k).
+  routing margins  brute force over (selected, unselected) pairs; constructed gaps.
   e4m3 codec       values fixed by the OCP 8-bit floating point format
                    definition (max 448, subnormal step 2^-9), round trips,
                    saturation, ties to even.
@@ -57,9 +58,18 @@ Readings where the pages are silent (each also listed in the design notes):
   * fp8 (E4M3FN, max 448): per-token per-128-column activation scales
     amax/448 in fp32 (1 when amax = 0), code = nearest E4M3 value of x/scale
     in fp32 with ties to even, saturating at +-448.  Weights arrive as codes
-    plus 128x128 block scales and mean code * scale.  The fp8 layer
-    quantises the rows entering both GEMMs (x, and h rounded to fp32) and
-    otherwise computes in float64.
+    plus 128x128 block scales and mean code * scale.  The reference of the
+    fp8 layer is the layer on those weights with exact activations
+    (act_quant=False).  The "DeepEP" section quantises the dispatched rows
+    only; the kernels also quantise h per 1x128 before the down GEMM, and
+    act_quant=True reproduces that form (x, and h rounded to fp32, quantised)
+    for a second, tighter comparison.
+
+Also pinned: act_quant by closed forms (activations on the E4M3 grid times a
+power-of-two scale quantise exactly; a hand-quantised 1x128 block of h), and
+routing_margins by brute force over every (selected, unselected) pair.  A
+plain C++ oracle (moe_ref.cpp) implements the same layer in loops; the pins
+run against both.
 """
 from __future__ import annotations
 
@@ -276,10 +286,11 @@ def swiglu_expert(a, w13, w2, act_quant=False):
     """One expert on rows a [n][d]: w13 [2F][d] holds gate rows [0, F) and up
     rows [F, 2F); w2 is [d][F].  out = (silu(a Wg^T) * (a Wu^T)) W2^T.
 
-    act_quant: the E4M3 form of the layer ("DeepEP" section, trick 1): the
-    rows entering each GEMM are first quantised per 1x128 block (the input
-    rows as fp32, h after rounding to fp32) and the GEMM reads their
-    dequantised values code * scale."""
+    act_quant: the quantised-activation form of the E4M3 kernels ("DeepEP"
+    section, trick 1, quantises the dispatched rows; the kernels also
+    quantise h): the rows entering each GEMM are first quantised per 1x128
+    block (the input rows as fp32, h after rounding to fp32) and the GEMM
+    reads their dequantised values code * scale."""
     a = np.asarray(a, dtype=np.float64)
     w13 = np.asarray(w13, dtype=np.float64)
     w2 = np.asarray(w2, dtype=np.float64)

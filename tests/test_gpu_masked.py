@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import moe_inputs as mi
-from moe_case import (TOL, Inputs, Weights, check_layer, check_route, cfg_of, host, rel_err, sample, say,
-                      y_values)
+from moe_case import (TOL, Inputs, Weights, _check_rows, check_layer, check_layer_all, check_route, cfg_of,
+                      fmt_err, host, rel_err, sample, say, y_values)
 from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -177,23 +177,15 @@ def test_masked_chain_against_oracle(name, T):
     r = run_masked(wl, inp, W)
     check_route(wl, inp, r)
     tok = check_masked_dispatch(wl, inp, r)
-    q = wl.weight_dtype == "fp8"
     worst = 0.0
     for e in np.unique(r["idx"]):
         rows = np.arange(e * T, e * T + r["count"][e])
-        ref = O.swiglu_expert(inp.xv[tok[rows]], *W.get_expert(int(e)), act_quant=q)
-        err = rel_err(r["eout"][rows], ref)
+        err = _check_rows(wl, r["eout"][rows],
+                          lambda q: O.swiglu_expert(inp.xv[tok[rows]], *W.get_expert(int(e)), act_quant=q), e)
         worst = max(worst, err)
-        assert err <= TOL[wl.weight_dtype], (e, err)
-    w_ref = O.gate_weights(inp.logits, r["idx"], wl)
-    y_ref = O.layer(inp.xv, inp.logits, inp.bias, wl, W.get_expert, W.get_shared if wl.num_shared else None,
-                    idx=r["idx"], w=w_ref, act_quant=q)
-    yv = y_values(wl, r["y"])
-    assert np.isfinite(yv).all()
-    e2 = rel_err(yv, y_ref)
-    assert e2 <= TOL[wl.weight_dtype], e2
+    e2, e2q = check_layer_all(wl, inp, r["y"], r["idx"], W)
     assert (r["count_after"] == 0).all()
-    say(f"  masked {name} T={T}: ffn err {worst:.2e}, y err {e2:.2e}")
+    say(f"  masked {name} T={T}: ffn err {worst:.2e}, y err {fmt_err(e2, e2q)}")
 
 
 def _moe_layer(wl, cfg, inp, W, ws):

@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import moe_inputs as mi
-from moe_case import (TOL, Inputs, Weights, check_dispatch, check_ffn, check_layer, check_route, cfg_of, host,
-                      run_chain, sample, say)
+from moe_case import (TOL, Inputs, Weights, check_dispatch, check_ffn, check_ffn_rows, check_layer,
+                      check_layer_all, check_route, cfg_of, fmt_err, host, run_chain, sample, say)
 from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -165,17 +165,9 @@ def test_layer_full_oracle(name, T):
     check_route(wl, inp, r)
     tok = check_dispatch(wl, inp, r)
     e1 = check_ffn(wl, inp, r, W, tok)
-    q = wl.weight_dtype == "fp8"
-    w_ref = O.gate_weights(inp.logits, r["idx"], wl)
-    y_ref = O.layer(inp.xv, inp.logits, inp.bias, wl, W.get_expert, W.get_shared if wl.num_shared else None,
-                    idx=r["idx"], w=w_ref, act_quant=q)
-    from moe_case import rel_err, y_values
-    yv = y_values(wl, r["y"])
-    assert np.isfinite(yv).all()
-    e2 = rel_err(yv, y_ref)
-    assert e2 <= TOL[wl.weight_dtype], e2
+    e2, e2q = check_layer_all(wl, inp, r["y"], r["idx"], W)
     assert (r["count_after"] == 0).all()
-    say(f"  layer {name} T={T}: ffn err {e1:.2e}, y err {e2:.2e}")
+    say(f"  layer {name} T={T}: ffn err {e1:.2e}, y err {fmt_err(e2, e2q)}")
 
 
 def _layer_via_moe_layer(wl, inp, W, ws=None):
@@ -224,6 +216,11 @@ BIG_LAYER = [("dsv3", 1), ("dsv3", 8), ("dsv3", 32), ("dsv3", 128), ("dsv3_fp8",
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,T", BIG_LAYER)
 def test_layer_full_size_sampled(name, T):
+    """Full-size layers: routing and dispatch whole; every touched expert on
+    its first and last rows and on both sides of the 16-, 32- and 128-row
+    chunk and tile boundaries (C++ oracle on the stored weights); the shared
+    expert on the first and last tokens; whole experts for a sample (numpy
+    oracle); y on sampled tokens through the dense per-token path."""
     wl = wl_of(name)
     inp = Inputs(wl, T)
     say(f"  generating weights for {name} T={T}")
@@ -235,6 +232,8 @@ def test_layer_full_size_sampled(name, T):
     check_route(wl, inp, r)
     tok = check_dispatch(wl, inp, r)
     rng = np.random.default_rng(T)
+    e0, n = check_ffn_rows(wl, inp, r, W, tok)
+    say(f"  {n} touched experts checked on their boundary rows: worst err {e0:.2e}")
     e1 = check_ffn(wl, inp, r, W, tok, max_experts=4, rng=rng)
     toks = sample(T, 8, rng)
     e2 = check_layer(wl, inp, r["y"], r["idx"], W, toks)

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 import moe_inputs as mi
-from moe_case import TOL, Inputs, Weights, check_dispatch, check_ffn, check_route, rel_err, run_chain, say, y_values
+from moe_case import (TOL, Inputs, Weights, check_dispatch, check_ffn, check_layer_all, check_route, fmt_err,
+                      rel_err, run_chain, say, y_values)
 from oracle import moe_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -55,16 +56,9 @@ def test_random_config(i):
     check_route(wl, inp, r)
     tok = check_dispatch(wl, inp, r)
     e1 = check_ffn(wl, inp, r, W, tok)
-    q = wl.weight_dtype == "fp8"
-    w_ref = O.gate_weights(inp.logits, r["idx"], wl)
-    y_ref = O.layer(inp.xv, inp.logits, inp.bias, wl, W.get_expert, W.get_shared if wl.num_shared else None,
-                    idx=r["idx"], w=w_ref, act_quant=q)
-    yv = y_values(wl, r["y"])
-    assert np.isfinite(yv).all()
-    e2 = rel_err(yv, y_ref)
-    assert e2 <= TOL[wl.weight_dtype], e2
+    e2, e2q = check_layer_all(wl, inp, r["y"], r["idx"], W)
     assert (r["count_after"] == 0).all()
-    say(f"  ffn err {e1:.2e}, y err {e2:.2e}")
+    say(f"  ffn err {e1:.2e}, y err {fmt_err(e2, e2q)}")
 
 
 # the validated maxima: E = 1024 experts, k = 64 slots (the whole wave picks),
@@ -91,11 +85,6 @@ def test_edge_maxima(wl, T):
     check_route(wl, inp, r)
     tok = check_dispatch(wl, inp, r)
     check_ffn(wl, inp, r, W, tok)
-    q = wl.weight_dtype == "fp8"
-    w_ref = O.gate_weights(inp.logits, r["idx"], wl)
-    y_ref = O.layer(inp.xv, inp.logits, inp.bias, wl, W.get_expert, W.get_shared if wl.num_shared else None,
-                    idx=r["idx"], w=w_ref, act_quant=q)
-    e2 = rel_err(y_values(wl, r["y"]), y_ref)
-    assert e2 <= TOL[wl.weight_dtype], e2
+    e2, e2q = check_layer_all(wl, inp, r["y"], r["idx"], W)
     assert (r["count_after"] == 0).all()
-    say(f"  y err {e2:.2e}")
+    say(f"  y err {fmt_err(e2, e2q)}")

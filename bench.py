@@ -11,11 +11,13 @@ would leave up to 256 MB of dirty lines in the Infinity Cache, whose
 write-back would then land inside the next timed step (about 55 us of extra
 HBM traffic that the layer itself never causes).
 
-The headline line is the Qwen3-30B-A3B-shaped decode layer at 128 tokens;
-the same JSON line carries the sweep over the other workloads and token
-counts (DeepSeek-V3-shaped decode in bf16 and E4M3, and the 4096-token
-prefill with Zipf-skewed routing), the roofline of the dominant kernel, and
-the CPU oracle timed on this host.
+The headline line is the DeepSeek-V3-shaped prefill layer at 4096 tokens
+with Zipf-skewed routing (the metric's 4096-token point, the largest
+workload that fits one GPU); the same JSON line carries the sweep over the
+other workloads and token counts (Qwen3-30B-A3B- and DeepSeek-V3-shaped
+decode at 1/8/32/128 tokens, the E4M3 layer at 32/128/512), the roofline of
+the dominant kernel, and the C++ CPU oracle timed on this host at one thread
+and at every thread of the host's share.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads ...]
 """
@@ -37,7 +39,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0                       # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}  # dense, published
 METRIC = "MoE-layer µs at 1/8/128/4096 tokens; achieved HBM GB/s & MFMA % of peak"
-HEADLINE = ("qwen3", 128)
+HEADLINE = ("dsv3_prefill", 4096)
 DEFAULT_SWEEP = {"qwen3": (1, 8, 32, 128), "dsv3": (1, 8, 32, 128), "dsv3_prefill": (4096,),
                  "dsv3_fp8": (32, 128, 512)}
 WORKLOAD_NAMES = {"qwen3": "qwen3-30b-a3b-moe-decode", "dsv3": "deepseek-v3-moe-decode",
@@ -302,53 +304,195 @@ def measure_router(layer, b, wl, steps, flush):
     return float(np.mean([s_.elapsed_time(e_) * 1e3 for s_, e_ in ev]))
 
 
-def cpu_baseline(wl, T, seed=0):
-    """The oracle, as it stands, on the headline workload: the whole layer
-    for T tokens, all weights read from the generator's bf16 values."""
+def measure_fused(layer, b, wl, steps, warmup, flush):
+    """Median us of moe_layer_fused (the whole layer in one persistent launch)
+    from the logits, and from the hidden states (the launch computes the
+    router logits itself), caches flushed before every call; None where the
+    fused launch does not cover the shape."""
+    import torch
     import moe_inputs as mi
-    from oracle import moe_oracle as O
+    import combine_experts_amd as M
+    if not M.moe_fused_supported(layer.cfg, b.T):
+        return None
+    nb = M.moe_fused_workspace_size(layer.cfg, b.T)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    if getattr(layer, "w_router", None) is None:
+        wr = mi.gen_router_weight(wl)
+        layer.w_router = torch.from_numpy(wr.view(np.int16) if wr.dtype == np.uint16 else wr).cuda()
+    out = {}
+    for key, lg, wr in (("fused_layer_us", b.logits, None), ("fused_from_hidden_us", None, layer.w_router)):
+        call = lambda: M.moe_layer_fused(layer.cfg, b.T, b.x, lg, wr, b.bias, layer.W, b.y, ws, nb)  # noqa: E731
+        for _ in range(warmup):
+            flush()
+            call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for s_, e_ in ev:
+            flush()
+            s_.record()
+            call()
+            e_.record()
+        torch.cuda.synchronize()
+        out[key] = round(float(np.median([s_.elapsed_time(e_) * 1e3 for s_, e_ in ev])), 2)
+    if int(ws[16:20].view(torch.int32).item()) != 0:
+        raise RuntimeError("moe_layer_fused: a grid-wide wait gave up (error word set)")
+    return out
+
+
+def host_threads():
+    """Threads of this host's share: OMP_NUM_THREADS when set, else the CPUs
+    this process may run on."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    x = mi.bf16_bits_to_f32(mi.gen_x(wl, T, seed)).astype(np.float64)
-    logits = mi.gen_logits(wl, T, seed)
+        return max(1, int(os.environ["OMP_NUM_THREADS"]))
+    except (KeyError, ValueError):
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, T, threads, budget_s=10.0, seed=0):
+    """The C++ oracle (oracle/moe_ref.cpp, as it stands) on the workload, on
+    this host's cores with `threads` threads, in the metric's unit (us per
+    layer call).
+
+    Routing and dispatch of all T tokens are timed whole.  The expert FFNs are
+    timed on a sample: touched experts taken at an even stride through the
+    row-count order (so the sample spans hot and cold experts), enough of them
+    for about budget_s seconds of work, and the shared expert on a
+    proportional slice of the tokens; both are scaled to the whole layer by
+    their FLOPs (the oracle's work is its multiply-adds: 6 d F per routed
+    row).  The combine is timed on a slice of the tokens and scaled by token
+    count.  Generating the sample experts' weights is input preparation and
+    is not timed; the oracle reads them in their bf16 / E4M3 storage form."""
+    import ctypes
+    import moe_inputs as mi
+    from oracle import moe_ref as R
+    L = R.lib()
+    E, k, d, F, Fs = wl.num_experts, wl.top_k, wl.d_model, wl.d_ff, wl.d_ff_shared
+    fp8 = wl.weight_dtype == "fp8"
+    c = R.config(wl, d_model=d, d_ff=F, d_ff_shared=Fs, act_dtype=wl.act_dtype, weight_dtype=wl.weight_dtype,
+                 act_quant=fp8)
+    x = np.ascontiguousarray(mi.gen_x(wl, T, seed))
+    logits = np.ascontiguousarray(mi.gen_logits(wl, T, seed))
     bias = mi.gen_bias(wl, seed)
-
-    def get_expert(e):
-        a = mi.bf16_bits_to_f32(mi.gen_weight(wl, "w13", e, seed)).astype(np.float64)
-        b = mi.bf16_bits_to_f32(mi.gen_weight(wl, "w2", e, seed)).astype(np.float64)
-        return a, b
-    # weight generation is input preparation: fetch every expert first
-    idx, _, _ = O.route(logits, bias, wl)
-    cache = {int(e): get_expert(int(e)) for e in np.unique(idx)}
-    # repeat for about ten seconds (at least 3 runs) and report the median
-    runs = []
-    t_start = time.perf_counter()
-    while len(runs) < 3 or (time.perf_counter() - t_start < 10.0 and len(runs) < 1000):
+    bias = np.ascontiguousarray(bias) if bias is not None else None
+    p = lambda a: a.ctypes.data if a is not None else None  # noqa: E731
+    idx = np.empty((T, k), np.int32)
+    tw = np.empty((T, k), np.float64)
+    t0 = time.perf_counter()
+    L.moe_ref_route(ctypes.byref(c), T, p(logits), p(bias), p(idx), p(tw))
+    t_route = time.perf_counter() - t0
+    counts, offsets = np.empty(E, np.int32), np.empty(E + 1, np.int32)
+    row_of, tok = np.empty((T, k), np.int32), np.empty(T * k, np.int32)
+    t0 = time.perf_counter()
+    L.moe_ref_dispatch(ctypes.byref(c), T, p(idx), p(counts), p(offsets), p(row_of), p(tok))
+    t_dispatch = time.perf_counter() - t0
+    # sample experts: an even stride through the touched experts by row count
+    rate = 2.5e9 * threads  # the oracle's FLOP/s per thread (measured), only to size the sample
+    want = budget_s * rate * 0.8
+    touched = sorted((int(counts[e]), e) for e in range(E) if counts[e] > 0)
+    per_row = 6.0 * d * F
+    total_rows = int(counts.sum())
+    n_pick = 1
+    while n_pick < len(touched) and per_row * total_rows * n_pick / len(touched) < want:
+        n_pick += 1
+    stride = len(touched) / n_pick
+    sample = sorted({touched[int(stride * (i + 0.5))][1] for i in range(n_pick)})
+    rows = int(sum(counts[e] for e in sample))
+    # the sample's dispatched rows and weights (untimed preparation)
+    sub_tok = np.concatenate([tok[offsets[e]:offsets[e + 1]] for e in sample]).astype(np.int32)
+    # a compact weight array holding only the sample experts (sample expert i
+    # in slot i), so that the whole layer's weights are never materialised
+    ns = len(sample)
+    cs = R.config(wl, d_model=d, d_ff=F, act_dtype=wl.act_dtype, weight_dtype=wl.weight_dtype, act_quant=fp8)
+    cs.num_experts, cs.top_k, cs.n_group, cs.topk_group = ns, 1, 1, 1
+    gw = [(mi.gen_weight(wl, "w13", e, seed), mi.gen_weight(wl, "w2", e, seed)) for e in sample]
+    if fp8:
+        a13 = np.ascontiguousarray(np.stack([g[0][0] for g in gw]))
+        a2 = np.ascontiguousarray(np.stack([g[1][0] for g in gw]))
+        s13 = np.ascontiguousarray(np.stack([g[0][1] for g in gw]))
+        s2 = np.ascontiguousarray(np.stack([g[1][1] for g in gw]))
+        W = R.RefWeights(p(a13), p(a2), None, None, p(s13), p(s2), None, None)
+    else:
+        a13 = np.ascontiguousarray(np.stack([g[0] for g in gw]))
+        a2 = np.ascontiguousarray(np.stack([g[1] for g in gw]))
+        W = R.RefWeights(p(a13), p(a2), None, None, None, None, None, None)
+    comp_off = np.zeros(ns + 1, np.int32)
+    for i, e in enumerate(sample):
+        comp_off[i + 1] = comp_off[i] + counts[e]
+    recv = np.empty((rows, d), np.float64)
+    eout = np.empty((rows, d), np.float64)
+    cg = R.config(wl, d_model=d, d_ff=F, act_dtype=wl.act_dtype, weight_dtype=wl.weight_dtype)
+    cg.top_k = 1
+    t0 = time.perf_counter()
+    L.moe_ref_gather(ctypes.byref(cg), rows, p(x), p(sub_tok), p(recv))
+    L.moe_ref_expert_ffn(ctypes.byref(cs), rows, p(recv), p(comp_off), ctypes.byref(W), None, p(eout), None, threads)
+    t_ffn = time.perf_counter() - t0
+    # shared expert on a proportional slice of the tokens
+    t_shared, Ts = 0.0, 0
+    if wl.num_shared:
+        Ts = max(1, int(round(T * n_pick / len(touched))))
+        a, b = mi.gen_weight(wl, "ws13", 0, seed), mi.gen_weight(wl, "ws2", 0, seed)
+        ch = R.config(wl, d_model=d, d_ff=Fs, act_dtype=wl.act_dtype, weight_dtype=wl.weight_dtype, act_quant=fp8)
+        ch.num_experts, ch.top_k, ch.n_group, ch.topk_group = 1, 1, 1, 1
+        keep = (np.ascontiguousarray(a[0] if fp8 else a), np.ascontiguousarray(b[0] if fp8 else b))
+        ks = (np.ascontiguousarray(a[1]), np.ascontiguousarray(b[1])) if fp8 else (None, None)
+        WS = R.RefWeights(p(keep[0]), p(keep[1]), None, None, p(ks[0]), p(ks[1]), None, None)
+        xs = np.ascontiguousarray(R._f64(mi.bf16_bits_to_f32(x[:Ts]) if x.dtype == np.uint16 else x[:Ts]))
+        so = np.empty((Ts, d), np.float64)
         t0 = time.perf_counter()
-        O.layer(x, logits, bias, wl, lambda e: cache[e])
-        runs.append(time.perf_counter() - t0)
-    return {"value": round(float(np.median(runs)) * 1e6, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
-            "sample": f"whole {WORKLOAD_NAMES[wl.name]} layer at {T} tokens (float64 numpy oracle: route, "
-                      f"dispatch, {len(cache)} experts, combine), median of {len(runs)} runs over "
-                      f"{time.perf_counter() - t_start:.1f} s, weight decode excluded"}
+        L.moe_ref_expert_ffn(ctypes.byref(ch), Ts, p(xs), p(np.array([0, Ts], np.int32)), ctypes.byref(WS), None,
+                             p(so), None, threads)
+        t_shared = time.perf_counter() - t0
+    # combine on a slice of the tokens (their rows taken from the sample output)
+    Tc = min(T, 256)
+    fake = np.ascontiguousarray(np.resize(eout, (Tc * k, d)))
+    rc = np.ascontiguousarray(np.arange(Tc * k, dtype=np.int32).reshape(Tc, k))
+    yc = np.empty((Tc, d), np.float64)
+    t0 = time.perf_counter()
+    L.moe_ref_combine(ctypes.byref(c), Tc, p(fake), p(rc), p(np.ascontiguousarray(tw[:Tc])), None, p(yc))
+    t_combine = time.perf_counter() - t0
+    routed_scale_up = total_rows / rows
+    est = (t_route + t_dispatch + t_ffn * routed_scale_up + (t_shared * T / Ts if Ts else 0.0)
+           + t_combine * T / Tc)
+    return {"value": round(est * 1e6, 1), "unit": "us", "cores": int(threads), "kind": "oracle",
+            "sample": (f"C++ oracle (double accumulation, {threads} thread{'s' if threads > 1 else ''}) on the "
+                       f"{WORKLOAD_NAMES[wl.name]} layer at {T} tokens: route and dispatch of all tokens timed "
+                       f"whole ({(t_route + t_dispatch) * 1e3:.1f} ms); expert FFNs timed on {ns} of "
+                       f"{len(touched)} touched experts ({rows} of {total_rows} routed rows, "
+                       f"{t_ffn:.2f} s) and scaled by rows; shared expert on {Ts} of {T} tokens "
+                       f"({t_shared:.2f} s) and combine on {Tc} tokens ({t_combine * 1e3:.1f} ms), scaled by "
+                       f"tokens; weight generation untimed"),
+            "timed_s": round(t_route + t_dispatch + t_ffn + t_shared + t_combine, 2)}
 
 
-def kernel_traffic(key):
+def kernel_traffic(key, source):
     """HBM bytes per launch measured with rocprofv3 counters, from the
     committed summary, if it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.md")
     if not os.path.exists(path):
         return None
-    src = open(os.path.join(ROOT, "combine_experts_amd", "csrc", "ffn.hip"), "rb").read()
+    src = open(os.path.join(ROOT, "combine_experts_amd", "csrc", source), "rb").read()
     digest = hashlib.sha256(src).hexdigest()[:16]
     for line in open(path):
-        m = re.match(r"\|\s*" + re.escape(key) + r"\s*\|\s*([0-9a-f]{16})\s*\|\s*([0-9.eE+]+)\s*\|", line)
+        m = re.match(r"\|\s*" + re.escape(key) + r"\s*\|\s*([0-9a-f]{16})\s*\|\s*([0-9.eE+,]+)\s*\|", line)
         if m and m.group(1) == digest:
-            return float(m.group(2))
+            return float(m.group(2).replace(",", ""))
     return None
+
+
+def uses_tiled(wl, T):
+    """The library's choice of grouped-GEMM kernel: the LDS-tiled one for
+    bf16 batches with 32 or more rows per expert on average, else the
+    weight-streaming one."""
+    return wl.weight_dtype == "bf16" and T * wl.top_k >= 32 * wl.num_experts
 
 
 def main():
@@ -464,10 +608,17 @@ def main():
                 rg_bytes = b_wl.num_experts * b_wl.d_model * ab + T * b_wl.d_model * ab + T * b_wl.num_experts * 4
                 ent["router_gemm_us"] = round(rg_us, 2)
                 ent["router_gemm_GBps"] = round(rg_bytes / rg_us / 1e3, 1)
+            fz = measure_fused(layer, b, b_wl, args.steps, args.warmup, flush)
+            if fz is not None:
+                ent.update(fz)
+                if "router_gemm_us" in ent:
+                    ent["router_gemm_plus_layer_us"] = round(ent["router_gemm_us"] + med, 2)
             sweep.append(ent)
             log(f"[bench] {name} T={T}: layer {med:.1f} us (HBM {ent['hbm_frac'] * 100:.1f}% of peak, "
                 f"roof {ent['hbm_roof_us']:.1f} us), phases {ent['phase_us_mean']}"
-                + (f", router GEMM {ent['router_gemm_us']} us" if "router_gemm_us" in ent else ""))
+                + (f", router GEMM {ent['router_gemm_us']} us" if "router_gemm_us" in ent else "")
+                + (f", fused {ent['fused_layer_us']} us ({ent['fused_from_hidden_us']} us from hidden states)"
+                   if "fused_layer_us" in ent else ""))
             if (name, T) == HEADLINE:
                 headline = (ent, layer_us, wall, gu_bytes, gu_flops, gu_us, b_wl)
             del b
@@ -496,14 +647,26 @@ def main():
                    "cache": "cold (1 GiB read before each step)"},
     }
     if gu_us:
-        out["roofline"] = {"kernel": "ffn_kernel gate/up+SwiGLU (moe_ffn_gate_up)", "bound": "hbm",
+        tiled = uses_tiled(hwl, ent["tokens"])
+        kname = ("gemm_tiled_kernel<true, 256> gate/up+SwiGLU (moe_ffn_gate_up)" if tiled
+                 else "ffn_kernel gate/up+SwiGLU (moe_ffn_gate_up)")
+        out["roofline"] = {"kernel": kname, "bound": "hbm",
                            "achieved": round(gu_bytes / gu_us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(gu_bytes / gu_us / 1e3 / HBM_PEAK_GBS, 4),
-                           "traffic": kernel_traffic(f"gate_up {ent['workload']} T={ent['tokens']}"),
-                           "alg_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 2)}
+                           "traffic": kernel_traffic(f"gate_up {ent['workload']} T={ent['tokens']}",
+                                                     "gemm_tiled.hip" if tiled else "ffn.hip"),
+                           "alg_bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_us, 2),
+                           "alg_flops_per_launch": gu_flops,
+                           "mfma_frac": round(gu_flops / gu_us / 1e6 / MFMA_PEAK_TFLOPS[hwl.weight_dtype], 4)}
     if not args.no_cpu_baseline and headline is not None:
-        log("[bench] timing the CPU oracle on the headline workload")
-        out["cpu_baseline"] = cpu_baseline(hwl, ent["tokens"])
+        nt = host_threads()
+        log(f"[bench] timing the C++ CPU oracle on the headline workload ({nt} threads, then 1)")
+        cb = cpu_baseline(hwl, ent["tokens"], nt)
+        one = cpu_baseline(hwl, ent["tokens"], 1)
+        cb["cpu_model"] = cpu_model()
+        cb["single_thread"] = {"value": one["value"], "unit": "us", "cores": 1, "sample": one["sample"],
+                               "timed_s": one["timed_s"]}
+        out["cpu_baseline"] = cb
     out["sweep"] = sweep
     print(json.dumps(out), flush=True)
 

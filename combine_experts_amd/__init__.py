@@ -9,7 +9,8 @@ from ._binding import (  # noqa: F401
     DTYPE, LIB_PATH, MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL,
     MOE_OK, SCORE, WEIGHT, MoeConfig, MoeError, MoeWeights, load_library, make_config, make_weights,
     moe_combine, moe_dispatch, moe_dispatch_rows, moe_expert_ffn, moe_ffn_down, moe_ffn_gate_up,
-    moe_ffn_workspace_size, moe_layer, moe_router_logits,
+    moe_ffn_workspace_size, moe_fused_supported, moe_fused_workspace_size, moe_layer, moe_layer_fused,
+    moe_router_logits,
     moe_route, moe_route_dispatch, moe_status_string, moe_workspace_size)
 
 load_library()

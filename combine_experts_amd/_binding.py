@@ -75,7 +75,12 @@ def load_library():
     lib.moe_combine.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_layer.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, sz, vp]
     lib.moe_router_logits.argtypes = [cp, i32, vp, vp, vp, vp]
-    for f in (lib.moe_route, lib.moe_dispatch, lib.moe_route_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up,
+    lib.moe_layer_fused.argtypes = [cp, i32, vp, vp, vp, vp, wp, vp, vp, sz, vp]
+    lib.moe_fused_workspace_size.argtypes = [cp, i32]
+    lib.moe_fused_workspace_size.restype = sz
+    lib.moe_fused_supported.argtypes = [cp, i32]
+    lib.moe_fused_supported.restype = i32
+    for f in (lib.moe_layer_fused, lib.moe_route, lib.moe_dispatch, lib.moe_route_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up,
               lib.moe_ffn_down, lib.moe_combine, lib.moe_layer, lib.moe_router_logits):
         f.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -187,3 +192,16 @@ def moe_layer(cfg, T, x, logits, bias, weights: MoeWeights, y, ws, ws_bytes, str
 def moe_router_logits(cfg, T, x, w_router, logits, stream=None):
     _check(load_library().moe_router_logits(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logits),
                                             _stream(stream)))
+
+
+def moe_layer_fused(cfg, T, x, logits, w_router, bias, weights: MoeWeights, y, ws, ws_bytes, stream=None):
+    _check(load_library().moe_layer_fused(ctypes.byref(cfg), T, _ptr(x), _ptr(logits), _ptr(w_router), _ptr(bias),
+                                          ctypes.byref(weights), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_fused_workspace_size(cfg: MoeConfig, max_tokens: int) -> int:
+    return load_library().moe_fused_workspace_size(ctypes.byref(cfg), max_tokens)
+
+
+def moe_fused_supported(cfg: MoeConfig, T: int) -> bool:
+    return bool(load_library().moe_fused_supported(ctypes.byref(cfg), T))

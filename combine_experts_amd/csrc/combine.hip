@@ -28,6 +28,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     for (int j = 0; j < 8; ++j) {
       r[j] = j0 + j < k ? rows[j0 + j] : 0;
       wj[j] = j0 + j < k ? w[j0 + j] : 0.f;
+      // a slot that got no row (counters left non-zero by an earlier failed
+      // call) reads row 0 with weight 0
+      if (r[j] < 0 || r[j] >= p.routed_rows) {
+        r[j] = 0;
+        wj[j] = 0.f;
+      }
     }
     f32x4_t v[8];
 #pragma unroll

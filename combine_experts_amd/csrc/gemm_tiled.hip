@@ -109,7 +109,7 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
       if (e < E) {
-        const int n = p.masked ? s_off[e] : s_off[e + 1] - s_off[e];
+        const int n = p.masked ? min(s_off[e], p.T) : s_off[e + 1] - s_off[e];
         if (n > 0) { ++cnt; items += ((n + BN - 1) / BN) * nt_r; }
       }
     }
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
       if (e < E) {
-        const int n = p.masked ? s_off[e] : s_off[e + 1] - s_off[e];
+        const int n = p.masked ? min(s_off[e], p.T) : s_off[e + 1] - s_off[e];
         if (n > 0) {
           s_grp[pc] = e;
           s_pre[pc] = pi;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
       const int g = __builtin_amdgcn_readfirstlane(s_grp[a]);
       local = item - __builtin_amdgcn_readfirstlane(s_pre[a]);
       it.rows0 = p.masked ? g * p.T : __builtin_amdgcn_readfirstlane(s_off[g]);
-      it.nrows = p.masked ? __builtin_amdgcn_readfirstlane(s_off[g])
+      it.nrows = p.masked ? min(__builtin_amdgcn_readfirstlane(s_off[g]), p.T)
                           : __builtin_amdgcn_readfirstlane(s_off[g + 1]) - it.rows0;
       mt = (it.nrows + BN - 1) / BN;
       it.K = p.K_r;

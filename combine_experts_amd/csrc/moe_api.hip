@@ -245,8 +245,61 @@ moe_status combine_impl(const moe_config* c, int32_t T, const float* eout, const
                         const float* w, const float* sout, void* y, int32_t* count, hipStream_t s) {
   CombineParams p{};
   p.T = T; p.E = c->num_experts; p.k = c->top_k; p.d = c->d_model; p.act_dtype = c->act_dtype;
+  p.routed_rows = (int)routed_rows(c, T);
   p.expert_out = eout; p.row_of = row_of; p.topk_w = w; p.shared_out = sout; p.y = y; p.expert_count = count;
   return hip_status(launch_combine(p, s));
+}
+
+// ---- the fused decode layer (fused.hip)
+
+constexpr int kFusedMaxT = 16, kFusedMaxSlots = 256, kFusedMaxE = 256;
+constexpr int kFusedSpinLimit = 1 << 22;  // ~0.2 s of s_sleep per grid barrier before giving up
+
+struct FusedLayout {
+  size_t sync, logits, eout, sout, ffn, total;
+};
+
+moe_config compact_of(const moe_config* c) {
+  moe_config cc = *c;
+  cc.masked_layout = 0;
+  return cc;
+}
+
+// sync words (four counters, then the error word) first, so that the zero
+// invariant carries over between calls of any size
+FusedLayout fused_layout(const moe_config* c, int64_t T) {
+  const moe_config cc = compact_of(c);
+  FusedLayout L{};
+  const size_t d = c->d_model;
+  size_t o = 0;
+  L.sync = o;   o = align256(o + 8 * sizeof(int));
+  L.logits = o; o = align256(o + (size_t)T * c->num_experts * sizeof(float));
+  L.eout = o;   o = align256(o + (size_t)T * c->top_k * d * sizeof(float));
+  L.sout = o;
+  if (c->num_shared) o = align256(o + (size_t)T * d * sizeof(float));
+  L.ffn = o;    o = align256(o + ffn_layout(&cc, T).total);
+  L.total = o;
+  return L;
+}
+
+// Launch shape of one pass of the fused layer (four waves), from the K-steps
+// of its items and its 16-column tiles (per: tiles per wave).
+bool fused_plan_of(int steps, int tiles_r, int tiles_s, int per, FusedPlan& pl) {
+  auto fits = [&](int fw) { return tiles_r % (fw * per) == 0 && tiles_s % (fw * per) == 0; };
+  if (steps >= 32 && fits(1)) { pl = {1, 4, false}; return true; }
+  if (steps >= 16 && steps % 2 == 0 && fits(2)) { pl = {2, 2, true}; return true; }
+  if (steps >= 1 && fits(4)) { pl = {4, 1, false}; return true; }
+  if (steps >= 4 && fits(1)) { pl = {1, 4, false}; return true; }
+  return false;
+}
+
+bool fused_plans(const moe_config* c, int32_t T, FusedPlan& a, FusedPlan& b) {
+  if (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_BF16) return false;
+  if (T < 1 || T > kFusedMaxT || T * c->top_k > kFusedMaxSlots || c->num_experts > kFusedMaxE) return false;
+  const int d = c->d_model, F = c->d_ff, Fs = c->num_shared ? c->d_ff_shared : F;
+  const int ns = c->num_shared;
+  if (!fused_plan_of(d / 128, F / 16, ns ? Fs / 16 : 0, 1, a)) return false;
+  return fused_plan_of((F < Fs ? F : Fs) / 128, d / 16, ns ? d / 16 : 0, 2, b);
 }
 
 moe_status check_weights(const moe_config* c, const moe_weights* W) {
@@ -491,6 +544,61 @@ moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const floa
   if ((st = dispatch_impl(cfg, T, x, idx, count, ticket, recv, recv_scale, offset, row_of, s)) != MOE_OK) return st;
   if ((st = ffn_impl(cfg, T, recv, recv_scale, offset, w, x, eout, sout, ffn_ws, s)) != MOE_OK) return st;
   return combine_impl(cfg, T, eout, row_of, tw, sout, y, count, s);
+}
+
+size_t moe_fused_workspace_size(const moe_config* cfg, int32_t max_tokens) {
+  if (check_config(cfg) != MOE_OK || max_tokens < 0) return 0;
+  return fused_layout(cfg, max_tokens).total;
+}
+
+int32_t moe_fused_supported(const moe_config* cfg, int32_t T) {
+  FusedPlan a, b;
+  return check_config(cfg) == MOE_OK && fused_plans(cfg, T, a, b) ? 1 : 0;
+}
+
+moe_status moe_layer_fused(const moe_config* cfg, int32_t T, const void* x, const float* logits, const void* w_router,
+                           const float* bias, const moe_weights* w, void* y, void* ws, size_t ws_bytes,
+                           void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if ((logits == nullptr) == (w_router == nullptr)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_weights(cfg, w)) != MOE_OK) return st;
+  if (!x || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (!all_aligned(x, y, ws) || (logits && !aligned16(logits)) || (w_router && !aligned16(w_router)) ||
+      (bias && !aligned16(bias)))
+    return MOE_ERR_INVALID_ARG;
+  FusedPlan pa, pb;
+  if (!fused_plans(cfg, T, pa, pb)) return MOE_ERR_UNSUPPORTED;
+  if (w_router && !router_gemv_fits(T, cfg->d_model, MOE_BF16)) return MOE_ERR_UNSUPPORTED;
+  const FusedLayout L = fused_layout(cfg, T);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const moe_config cc = compact_of(cfg);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  FusedParams fp{};
+  float* lws = reinterpret_cast<float*>(b + L.logits);
+  fp.r = route_params(&cc, T, w_router ? lws : logits, bias, nullptr, nullptr, nullptr, nullptr);
+  float* eout = reinterpret_cast<float*>(b + L.eout);
+  float* sout = cc.num_shared ? reinterpret_cast<float*>(b + L.sout) : nullptr;
+  void* ffn_ws = b + L.ffn;
+  fp.a = gate_up_params(&cc, T, x, nullptr, nullptr, w, x, ffn_ws);
+  fp.a.tiles_r /= pa.fw;
+  fp.a.tiles_s /= pa.fw;
+  fp.b = down_params(&cc, T, nullptr, w, ffn_ws, eout, sout);
+  fp.b.tiles_r /= 2 * pb.fw;
+  fp.b.tiles_s /= 2 * pb.fw;
+  fp.x = x;
+  fp.w_router = w_router;
+  fp.logits_ws = lws;
+  fp.d = cc.d_model;
+  fp.expert_out = eout;
+  fp.shared_out = sout;
+  fp.y = y;
+  fp.sync = reinterpret_cast<int*>(b + L.sync);
+  fp.err = fp.sync + 4;
+  fp.spin_limit = kFusedSpinLimit;
+  return hip_status(launch_fused(fp, pa, pb, (hipStream_t)stream));
 }
 
 const char* moe_status_string(moe_status status) {

@@ -73,6 +73,7 @@ struct FfnParams {
 
 struct CombineParams {
   int T, E, k, d, act_dtype;
+  int routed_rows;  // rows of expert_out: slots whose row_of lies outside contribute nothing
   const float* expert_out;
   const int* row_of;
   const float* topk_w;
@@ -81,7 +82,38 @@ struct CombineParams {
   int* expert_count;
 };
 
+// The whole layer for a handful of tokens in one persistent launch.  r: the
+// routing rule (r.logits: the layer's logits, or logits_ws when the launch
+// computes them from x and w_router).  a, b: the gate/up and down passes in
+// the compact layout; their offsets come from the launch's own routing and a
+// reads the tokens themselves (no dispatch copy).  sync: four counters, zero
+// between calls (grid barriers after the router GEMM, the gate/up pass and
+// the down pass, then an exit count; the last workgroup out zeroes them).
+// err: set to 1 when a bounded wait gives up (the results are then invalid).
+struct FusedParams {
+  RouteParams r;
+  FfnParams a, b;
+  const void* x;
+  const void* w_router;  // nullptr: r.logits is an input
+  float* logits_ws;
+  int d;
+  const float* expert_out;
+  const float* shared_out;
+  void* y;
+  int* sync;
+  int* err;
+  int spin_limit;
+};
+
+// Launch shape of one pass of the fused layer (four waves): FW column waves
+// x KS reduction splits, activation tiles shared through LDS or not.
+struct FusedPlan {
+  int fw, ks;
+  bool share;
+};
+
 hipError_t launch_route(const RouteParams& p, hipStream_t stream);
+hipError_t launch_fused(const FusedParams& p, const FusedPlan& a, const FusedPlan& b, hipStream_t stream);
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream);
 // gated: gate/up + SwiGLU pass (output dtype: bf16, or E4M3 with scales for
 // E4M3 weights, or f32); otherwise the down pass (f32 output).  routed_rows

@@ -95,39 +95,6 @@ hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
 // its part of the token into the rows the token reserved.
 // ---------------------------------------------------------------------------
 
-// Exclusive prefix sum of cnt[0..E) into off[0..E] (LDS), 256 threads, E <= 1024.
-__device__ void block_offsets(const int* cnt, int E, int* off, int* wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int v[4];
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    v[i] = e < E ? cnt[e] : 0;
-    local += v[i];
-  }
-  // inclusive scan of `local` across the wave
-  int inc = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) wsum[wid] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wid; ++w) base += wsum[w];
-  int run = base + inc - local;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
-    if (e < E) off[e] = run;
-    run += v[i];
-  }
-  if (tid == 255) off[E] = run;  // E <= 1024 = 256 * 4, so thread 255 ends the scan
-  __syncthreads();
-}
-
 // Grid (T, column blocks).  Compact layout: rows follow from the offsets
 // scan; masked layout: row = expert * T + ticket, no scan.  Plain rows: a
 // block copies 4096 bytes of its token (256 threads x 16 B); E4M3 rows: a
@@ -167,10 +134,13 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
   if (!p.masked) {  // uniform: the scan's barriers are met by every thread
     block_offsets(p.expert_count, p.E, off, wsum);
     if (blockIdx.x == 0 && blockIdx.y == 0)
-      for (int e = tid; e <= p.E; e += 256) p.expert_offset[e] = off[e];
+      for (int e = tid; e <= p.E; e += 256) p.expert_offset[e] = min(off[e], p.routed_rows);
   }
   if (tid < k) {
-    const int r = p.masked ? my_e * p.T + my_ticket : off[my_e] + my_ticket;
+    int r = p.masked ? my_e * p.T + my_ticket : off[my_e] + my_ticket;
+    // counters left non-zero by an earlier failed call: a slot whose row
+    // falls outside its expert's rows or the buffer writes nothing
+    if ((p.masked && my_ticket >= p.T) || r >= p.routed_rows) r = -1;
     rows[tid] = r;
     if (blockIdx.y == 0) p.row_of[(size_t)t * k + tid] = r;
   }
@@ -181,7 +151,8 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
   if constexpr (!QUANT) {
     if (piece < pieces)
       for (int j = 0; j < nrows; ++j)
-        reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d * EB)[piece] = v;
+        if (rows[j] >= 0)
+          reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d * EB)[piece] = v;
   } else {
     if (blk < nb) {  // uniform per wave
       const float v0 = bf16_bits_to_f32(pair & 0xFFFFu), v1 = bf16_bits_to_f32(pair >> 16);
@@ -192,6 +163,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
       const uint32_t c0 = f32_to_e4m3(v0 / scale), c1 = f32_to_e4m3(v1 / scale);
       const uint16_t codes = (uint16_t)(c0 | (c1 << 8));
       for (int j = 0; j < nrows; ++j) {
+        if (rows[j] < 0) continue;
         uint8_t* dst = static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d;
         reinterpret_cast<uint16_t*>(dst + blk * 128)[lane] = codes;
         if (lane == 0) p.recv_scale[(size_t)rows[j] * nb + blk] = scale;

@@ -6,6 +6,39 @@
 
 namespace moe {
 
+// Exclusive prefix sum of cnt[0..E) into off[0..E] (LDS), 256 threads, E <= 1024.
+__device__ inline void block_offsets(const int* cnt, int E, int* off, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int v[4];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    v[i] = e < E ? cnt[e] : 0;
+    local += v[i];
+  }
+  // inclusive scan of `local` across the wave
+  int inc = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wid] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += wsum[w];
+  int run = base + inc - local;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) off[e] = run;
+    run += v[i];
+  }
+  if (tid == 255) off[E] = run;  // E <= 1024 = 256 * 4, so thread 255 ends the scan
+  __syncthreads();
+}
+
 // LDS floats one routing wave needs: keys[E], scores[E], and 384 words of
 // group and selection scratch.
 __host__ __device__ inline int route_lds_floats(int E) { return 2 * E + 384; }
@@ -31,22 +64,17 @@ __device__ __forceinline__ uint32_t ord(float f) {
 
 __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
 
-// Routes token bid * NW + w with wave w of an NW-wave block; smem holds
-// route_lds_floats(E) floats per wave.  Returns, in lane j < k, the
-// masked-layout row of the token's slot j (when p.fuse; 0 otherwise), and -1
-// in every lane when the token is past T.  With TICKET = false the slots take
-// no ticket here (the caller reserves them) and lane j < k returns the
-// expert of slot j instead.
-template <int KPL, int NW, bool TICKET = true>
-__device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* smem) {
+// Selection of token t by the calling wave, with no side effects: lane j < k
+// gets the expert of slot j (slots by descending key) in my_idx and its gate
+// weight (routed_scale applied) in my_w.  kbuf holds route_lds_floats(E)
+// floats of this wave's LDS.
+template <int KPL>
+__device__ __forceinline__ void route_select(const RouteParams& p, int t, float* kbuf, int& my_idx, float& my_w) {
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int t = bid * NW + wid;
   const int E = p.E;
   // per-wave LDS: keys[E], scores[E], group scores[64], group chosen[64],
   // chosen (key, index) in index order [64 + 64], chosen (index, score) in
   // output order [64 + 64]
-  float* kbuf = smem + wid * route_lds_floats(E);
   float* sbuf = kbuf + E;
   float* gbuf = sbuf + E;
   float* cbuf = gbuf + 64;
@@ -54,7 +82,6 @@ __device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* 
   int* ce = reinterpret_cast<int*>(cu + 64);
   int* oe = ce + 64;
   float* os = reinterpret_cast<float*>(oe + 64);
-  if (t >= p.T) return -1;  // uniform per wave; no block barrier is used below
 
   const float* lg = p.logits + (size_t)t * E;
   float key[KPL];
@@ -194,7 +221,7 @@ __device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* 
   }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  int my_idx = 0;
+  my_idx = 0;
   float my_s = 0.f;
   if (lane < k) {
     my_idx = oe[lane];
@@ -244,8 +271,26 @@ __device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* 
       w = expf(my_s - sm) / den;
     }
   }
-  w *= p.routed_scale;
+  my_w = w * p.routed_scale;
+}
 
+// Routes token bid * NW + w with wave w of an NW-wave block; smem holds
+// route_lds_floats(E) floats per wave.  Returns, in lane j < k, the
+// masked-layout row of the token's slot j (when p.fuse; 0 otherwise), and -1
+// in every lane when the token is past T.  With TICKET = false the slots take
+// no ticket here (the caller reserves them) and lane j < k returns the
+// expert of slot j instead.
+template <int KPL, int NW, bool TICKET = true>
+__device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int t = bid * NW + wid;
+  float* kbuf = smem + wid * route_lds_floats(p.E);
+  if (t >= p.T) return -1;  // uniform per wave; no block barrier is used below
+  int my_idx;
+  float w;
+  route_select<KPL>(p, t, kbuf, my_idx, w);
+  const int k = p.k;
   int my_row = 0;
   if (lane < k) {
     const size_t o = (size_t)t * k + lane;
@@ -255,7 +300,7 @@ __device__ __forceinline__ int route_body(const RouteParams& p, int bid, float* 
       const int tk = atomicAdd(p.expert_count + my_idx, 1);
       if (p.ticket) p.ticket[o] = tk;
       if (p.fuse) {
-        my_row = my_idx * p.T + tk;
+        my_row = tk < p.T ? my_idx * p.T + tk : -1;  // -1: stale counters, the slot writes no row
         p.row_of[o] = my_row;
       }
     } else {
@@ -292,7 +337,8 @@ __device__ __forceinline__ void route_dispatch_block(const RouteParams& p, int t
     for (int c = tid; c < pieces; c += 64 * NWAVE) {
       const i32x4_t v = src[c];
       for (int j = 0; j < k; ++j)
-        reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows_s[j] * d * eb)[c] = v;
+        if (rows_s[j] >= 0)
+          reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows_s[j] * d * eb)[c] = v;
     }
     return;
   }
@@ -310,6 +356,7 @@ __device__ __forceinline__ void route_dispatch_block(const RouteParams& p, int t
     const uint16_t codes = (uint16_t)(c0 | (c1 << 8));
     for (int j = 0; j < nrows; ++j) {
       const int r = rows_s[j];
+      if (r < 0) continue;  // stale counters: the slot writes no row
       uint8_t* dst = static_cast<uint8_t*>(p.recv) + (size_t)r * d;
       reinterpret_cast<uint16_t*>(dst + b * 128)[lane] = codes;
       if (lane == 0) p.recv_scale[(size_t)r * nb + b] = scale;

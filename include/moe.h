@@ -151,7 +151,12 @@ size_t moe_ffn_workspace_size(const moe_config* cfg, int32_t max_tokens);
 /* Bytes of device workspace moe_layer needs for up to max_tokens tokens
  * (0 on an invalid config or max_tokens < 0).  The caller zero-fills the
  * workspace once after allocating it; the layer leaves its counters at zero
- * when it returns, so the same workspace serves every later call. */
+ * when it returns, so the same workspace serves every later call with the
+ * same config (or one with no more experts: the counters are the first E
+ * words).  After a call that returned anything but MOE_OK the counters may
+ * be left non-zero: zero-fill the workspace again before the next call.  (The kernels bound
+ * every row they write or read by the buffers' sizes, so a stale workspace
+ * gives wrong results, never an access outside the buffers.) */
 size_t moe_workspace_size(const moe_config* cfg, int32_t max_tokens);
 
 /*
@@ -161,7 +166,8 @@ size_t moe_workspace_size(const moe_config* cfg, int32_t max_tokens);
  *   topk_idx     [T][k] int32 out: chosen experts, descending key
  *   topk_w       [T][k] fp32 out: gate weights (sum = routed_scale)
  *   expert_count [E] int32 in/out: MUST be zero on entry; on exit holds the
- *                number of (token, slot) pairs routed to each expert
+ *                number of (token, slot) pairs routed to each expert (moe_combine
+ *                zeroes it again; after a failed call the caller must)
  *   ticket       [T][k] int32 out: the token's slot within its expert's rows,
  *                taken with an atomic add on expert_count; tickets of one
  *                expert are a permutation of 0..count-1 in an unspecified
@@ -287,6 +293,40 @@ moe_status moe_router_logits(const moe_config* cfg, int32_t T, const void* x, co
 moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const float* logits,
                      const float* bias, const moe_weights* w, void* y, void* ws, size_t ws_bytes,
                      void* stream);
+
+/*
+ * moe_layer_fused: the whole layer for a handful of tokens in ONE persistent
+ * launch ("DeepSeek MoE Serving: Where Expert-Parallel All-to-All Time
+ * Goes", section "The batch-scaling curve is the diagnostic": a fused MoE
+ * kernel running dispatch, both expert GEMMs and combine in one kernel;
+ * "7.13 Serving Mixture-of-Experts", "DeepEP" trick 3: at decode batch sizes
+ * the per-layer launch overhead can rival the work).  Optionally it starts
+ * from the hidden states and computes the router logits itself (the
+ * moe_ep_layer listing's x @ router_w^T).
+ *   Exactly one of logits ([T][E] fp32, as for moe_layer) and w_router
+ *   ([E][d] bf16, as for moe_router_logits) is non-NULL; with w_router the
+ *   logits are computed in the launch, with moe_router_logits' arithmetic.
+ *   x, bias, w, y: as for moe_layer.  masked_layout is ignored.
+ *   ws, ws_bytes: workspace of at least moe_fused_workspace_size(cfg, T)
+ *   bytes, zero-filled once by the caller; the launch leaves its counters at
+ *   zero, so the same workspace serves every later call.  The int at byte 16
+ *   of ws is set to 1 (and never cleared by the library) when one of the
+ *   launch's bounded grid-wide waits gave up: the results of that call are
+ *   then invalid.
+ *   Supported (else MOE_ERR_UNSUPPORTED, nothing launched): bf16 activations
+ *   and weights, 1 <= T <= 16, T*k <= 256, E <= 256, d <= 16384 when w_router
+ *   is given (moe_fused_supported tells).  Routing, weights and rows follow
+ *   moe_layer exactly; an expert's rows are ordered by token (no atomics),
+ *   so the output is reproducible bit for bit run to run.
+ *   The launch keeps one workgroup on every CU and synchronises them with
+ *   grid-wide barriers: it must not share the GPU with another launch that
+ *   occupies every CU for long (it waits for CUs, within its bound).
+ */
+moe_status moe_layer_fused(const moe_config* cfg, int32_t T, const void* x, const float* logits, const void* w_router,
+                           const float* bias, const moe_weights* w, void* y, void* ws, size_t ws_bytes,
+                           void* stream);
+size_t moe_fused_workspace_size(const moe_config* cfg, int32_t max_tokens);
+int32_t moe_fused_supported(const moe_config* cfg, int32_t T);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status status);

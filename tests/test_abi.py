@@ -162,3 +162,29 @@ def test_router_logits_argument_checks(M):
     with pytest.raises(M.MoeError) as e:  # E not a multiple of 64
         M.moe_router_logits(dsv3(M, num_experts=96, n_group=8, topk_group=4), 4, 16, 16, 16, stream=0)
     assert e.value.status == M.MOE_ERR_UNSUPPORTED
+
+
+def test_fused_layer_support_and_argument_checks(M):
+    """moe_layer_fused covers bf16 layers of 1-16 tokens with up to 256
+    experts, and rejects everything else before launching."""
+    cfg = dsv3(M)
+    assert M.moe_fused_supported(cfg, 1) and M.moe_fused_supported(cfg, 16)
+    assert not M.moe_fused_supported(cfg, 17) and not M.moe_fused_supported(cfg, 0)
+    assert not M.moe_fused_supported(dsv3(M, weight_dtype="fp8"), 8)
+    assert not M.moe_fused_supported(dsv3(M, num_experts=512, n_group=8), 8)
+    nb = M.moe_fused_workspace_size(cfg, 8)
+    assert nb > 0 and M.moe_fused_workspace_size(cfg, 16) > nb
+    W = M.MoeWeights(16, 16, 16, 16)
+    with pytest.raises(M.MoeError) as e:  # both logits and router weight given
+        M.moe_layer_fused(cfg, 8, 16, 16, 16, None, W, 16, 16, nb, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:  # neither
+        M.moe_layer_fused(cfg, 8, 16, None, None, None, W, 16, 16, nb, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer_fused(cfg, 17, 16, 16, None, None, W, 16, 16, 1 << 40, stream=0)
+    assert e.value.status == M.MOE_ERR_UNSUPPORTED
+    with pytest.raises(M.MoeError) as e:
+        M.moe_layer_fused(cfg, 8, 16, 16, None, None, W, 16, 16, nb - 1, stream=0)
+    assert e.value.status == M.MOE_ERR_WORKSPACE_TOO_SMALL
+    M.moe_layer_fused(cfg, 0, None, None, None, None, W, None, None, 0, stream=0)  # T = 0: nothing to do

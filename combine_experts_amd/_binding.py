@@ -14,7 +14,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_hip.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP, MOE_ERR_SCRATCH_LIMIT = range(6)
 SCORE = {"softmax": 0, "sigmoid": 1}
 WEIGHT = {"norm_sum": 0, "softmax_selected": 1}
 DTYPE = {"f32": 0, "bf16": 1, "fp8": 2}
@@ -80,7 +80,10 @@ def load_library():
     lib.moe_fused_workspace_size.restype = sz
     lib.moe_fused_supported.argtypes = [cp, i32]
     lib.moe_fused_supported.restype = i32
-    for f in (lib.moe_layer_fused, lib.moe_route, lib.moe_dispatch, lib.moe_route_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up,
+    lib.moe_layer_static.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp]
+    lib.moe_layer_static_max_bytes.argtypes = []
+    lib.moe_layer_static_max_bytes.restype = sz
+    for f in (lib.moe_layer_fused, lib.moe_layer_static, lib.moe_route, lib.moe_dispatch, lib.moe_route_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up,
               lib.moe_ffn_down, lib.moe_combine, lib.moe_layer, lib.moe_router_logits):
         f.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -192,6 +195,15 @@ def moe_layer(cfg, T, x, logits, bias, weights: MoeWeights, y, ws, ws_bytes, str
 def moe_router_logits(cfg, T, x, w_router, logits, stream=None):
     _check(load_library().moe_router_logits(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logits),
                                             _stream(stream)))
+
+
+def moe_layer_static(cfg, T, x, logits, bias, weights: MoeWeights, y, stream=None):
+    _check(load_library().moe_layer_static(ctypes.byref(cfg), T, _ptr(x), _ptr(logits), _ptr(bias),
+                                           ctypes.byref(weights), _ptr(y), _stream(stream)))
+
+
+def moe_layer_static_max_bytes() -> int:
+    return load_library().moe_layer_static_max_bytes()
 
 
 def moe_layer_fused(cfg, T, x, logits, w_router, bias, weights: MoeWeights, y, ws, ws_bytes, stream=None):

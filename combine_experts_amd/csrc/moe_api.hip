@@ -608,6 +608,7 @@ const char* moe_status_string(moe_status status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: configuration not supported by the kernels";
     case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL: workspace below the required size";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    case MOE_ERR_SCRATCH_LIMIT: return "MOE_ERR_SCRATCH_LIMIT: the call needs more than the library's static scratch";
   }
   return "unknown moe_status";
 }

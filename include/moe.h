@@ -38,8 +38,9 @@
  *     is the fastest-varying one.  Device pointers must be 16-byte aligned.
  *   - Element types: MOE_F32 = IEEE binary32, MOE_BF16 = bfloat16 bit
  *     patterns (uint16), MOE_FP8_E4M3 = OCP E4M3FN bytes (max 448, no inf).
- *   - The library holds no mutable global state: calls on different streams
- *     with different buffers may run concurrently.
+ *   - Apart from the scratch of moe_layer_static, the library holds no
+ *     mutable global state: calls on different streams with different
+ *     buffers may run concurrently.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -56,7 +57,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1,         /* null/misaligned pointer, bad size or config */
   MOE_ERR_UNSUPPORTED = 2,         /* valid config outside what the kernels cover */
   MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes below the matching *_workspace_size */
-  MOE_ERR_HIP = 4                  /* a HIP launch failed */
+  MOE_ERR_HIP = 4,                 /* a HIP launch failed */
+  MOE_ERR_SCRATCH_LIMIT = 5        /* moe_layer_static: the call needs more than its static scratch */
 } moe_status;
 
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
@@ -327,6 +329,28 @@ moe_status moe_layer_fused(const moe_config* cfg, int32_t T, const void* x, cons
                            void* stream);
 size_t moe_fused_workspace_size(const moe_config* cfg, int32_t max_tokens);
 int32_t moe_fused_supported(const moe_config* cfg, int32_t T);
+
+/*
+ * moe_layer_static: moe_layer without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * intermediates live in a scratch array inside the library, one copy of
+ * moe_layer_static_max_bytes() bytes (64 MiB) per GPU, held until the process
+ * ends.  Arguments and results are those of moe_layer.
+ *   Returns MOE_ERR_SCRATCH_LIMIT, launching nothing, when the call needs more
+ *   than that (moe_workspace_size(cfg, T) > moe_layer_static_max_bytes():
+ *   e.g. the DeepSeek-V3-shaped bf16 layer fits up to about 160 tokens in
+ *   the compact layout, the Qwen3-30B-A3B-shaped one about 600).
+ *   Every call on a GPU shares that GPU's scratch, whatever its config.  The
+ *   library keeps the routing counters zero between calls (a fill kernel on a
+ *   device's first call, after a call that returned an error, and before a
+ *   call whose config has more experts than the previous call's); calls that
+ *   overlap on one GPU (other streams or threads) race on the scratch and
+ *   must be serialised by the caller.
+ */
+moe_status moe_layer_static(const moe_config* cfg, int32_t T, const void* x, const float* logits,
+                            const float* bias, const moe_weights* w, void* y, void* stream);
+size_t moe_layer_static_max_bytes(void);
 
 /* Static, human-readable name of a status code. */
 const char* moe_status_string(moe_status status);

@@ -348,13 +348,21 @@ def host_threads():
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family/model numbers
+    (a virtualised host may print only the vendor's brand in the name)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                key, val = (s.strip() for s in line.split(":", 1))
+                info.setdefault(key, val)
+            elif info:
+                break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    nums = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    return f"{name} ({', '.join(nums)})" if nums else name
 
 
 def cpu_baseline(wl, T, threads, budget_s=10.0, seed=0):
@@ -395,7 +403,7 @@ def cpu_baseline(wl, T, threads, budget_s=10.0, seed=0):
     L.moe_ref_dispatch(ctypes.byref(c), T, p(idx), p(counts), p(offsets), p(row_of), p(tok))
     t_dispatch = time.perf_counter() - t0
     # sample experts: an even stride through the touched experts by row count
-    rate = 2.5e9 * threads  # the oracle's FLOP/s per thread (measured), only to size the sample
+    rate = 4.5e9 * threads  # the oracle's FLOP/s per thread (measured), only to size the sample
     want = budget_s * rate * 0.8
     touched = sorted((int(counts[e]), e) for e in range(E) if counts[e] > 0)
     per_row = 6.0 * d * F

@@ -252,11 +252,10 @@ moe_status combine_impl(const moe_config* c, int32_t T, const float* eout, const
 
 // ---- the fused decode layer (fused.hip)
 
-constexpr int kFusedMaxT = 16, kFusedMaxSlots = 256, kFusedMaxE = 256;
-constexpr int kFusedSpinLimit = 1 << 22;  // ~0.2 s of s_sleep per grid barrier before giving up
+constexpr int kFusedSpinLimit = 1 << 22;  // ~0.1 s of s_sleep per grid barrier before giving up
 
 struct FusedLayout {
-  size_t sync, logits, eout, sout, ffn, total;
+  size_t sync, logits, h, total;
 };
 
 moe_config compact_of(const moe_config* c) {
@@ -266,40 +265,22 @@ moe_config compact_of(const moe_config* c) {
 }
 
 // sync words (four counters, then the error word) first, so that the zero
-// invariant carries over between calls of any size
+// invariant carries over between calls of any size; then the router's
+// logits [T][E] f32 and h: [T*k][F] bf16 (routed slots), [T][Fs] bf16
+// (shared expert)
 FusedLayout fused_layout(const moe_config* c, int64_t T) {
-  const moe_config cc = compact_of(c);
   FusedLayout L{};
-  const size_t d = c->d_model;
   size_t o = 0;
   L.sync = o;   o = align256(o + 8 * sizeof(int));
   L.logits = o; o = align256(o + (size_t)T * c->num_experts * sizeof(float));
-  L.eout = o;   o = align256(o + (size_t)T * c->top_k * d * sizeof(float));
-  L.sout = o;
-  if (c->num_shared) o = align256(o + (size_t)T * d * sizeof(float));
-  L.ffn = o;    o = align256(o + ffn_layout(&cc, T).total);
+  L.h = o;      o = align256(o + (size_t)T * c->top_k * c->d_ff * 2 + (c->num_shared ? (size_t)T * c->d_ff_shared * 2 : 0));
   L.total = o;
   return L;
 }
 
-// Launch shape of one pass of the fused layer (four waves), from the K-steps
-// of its items and its 16-column tiles (per: tiles per wave).
-bool fused_plan_of(int steps, int tiles_r, int tiles_s, int per, FusedPlan& pl) {
-  auto fits = [&](int fw) { return tiles_r % (fw * per) == 0 && tiles_s % (fw * per) == 0; };
-  if (steps >= 32 && fits(1)) { pl = {1, 4, false}; return true; }
-  if (steps >= 16 && steps % 2 == 0 && fits(2)) { pl = {2, 2, true}; return true; }
-  if (steps >= 1 && fits(4)) { pl = {4, 1, false}; return true; }
-  if (steps >= 4 && fits(1)) { pl = {1, 4, false}; return true; }
-  return false;
-}
-
-bool fused_plans(const moe_config* c, int32_t T, FusedPlan& a, FusedPlan& b) {
+bool fused_ok(const moe_config* c, int32_t T) {
   if (c->act_dtype != MOE_BF16 || c->weight_dtype != MOE_BF16) return false;
-  if (T < 1 || T > kFusedMaxT || T * c->top_k > kFusedMaxSlots || c->num_experts > kFusedMaxE) return false;
-  const int d = c->d_model, F = c->d_ff, Fs = c->num_shared ? c->d_ff_shared : F;
-  const int ns = c->num_shared;
-  if (!fused_plan_of(d / 128, F / 16, ns ? Fs / 16 : 0, 1, a)) return false;
-  return fused_plan_of((F < Fs ? F : Fs) / 128, d / 16, ns ? d / 16 : 0, 2, b);
+  return fused_shape_ok(T, c->top_k, c->num_experts, c->d_model, c->d_ff, c->num_shared ? c->d_ff_shared : 0);
 }
 
 moe_status check_weights(const moe_config* c, const moe_weights* W) {
@@ -552,8 +533,7 @@ size_t moe_fused_workspace_size(const moe_config* cfg, int32_t max_tokens) {
 }
 
 int32_t moe_fused_supported(const moe_config* cfg, int32_t T) {
-  FusedPlan a, b;
-  return check_config(cfg) == MOE_OK && fused_plans(cfg, T, a, b) ? 1 : 0;
+  return check_config(cfg) == MOE_OK && fused_ok(cfg, T) ? 1 : 0;
 }
 
 moe_status moe_layer_fused(const moe_config* cfg, int32_t T, const void* x, const float* logits, const void* w_router,
@@ -569,8 +549,7 @@ moe_status moe_layer_fused(const moe_config* cfg, int32_t T, const void* x, cons
   if (!all_aligned(x, y, ws) || (logits && !aligned16(logits)) || (w_router && !aligned16(w_router)) ||
       (bias && !aligned16(bias)))
     return MOE_ERR_INVALID_ARG;
-  FusedPlan pa, pb;
-  if (!fused_plans(cfg, T, pa, pb)) return MOE_ERR_UNSUPPORTED;
+  if (!fused_ok(cfg, T)) return MOE_ERR_UNSUPPORTED;
   if (w_router && !router_gemv_fits(T, cfg->d_model, MOE_BF16)) return MOE_ERR_UNSUPPORTED;
   const FusedLayout L = fused_layout(cfg, T);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -579,26 +558,23 @@ moe_status moe_layer_fused(const moe_config* cfg, int32_t T, const void* x, cons
   FusedParams fp{};
   float* lws = reinterpret_cast<float*>(b + L.logits);
   fp.r = route_params(&cc, T, w_router ? lws : logits, bias, nullptr, nullptr, nullptr, nullptr);
-  float* eout = reinterpret_cast<float*>(b + L.eout);
-  float* sout = cc.num_shared ? reinterpret_cast<float*>(b + L.sout) : nullptr;
-  void* ffn_ws = b + L.ffn;
-  fp.a = gate_up_params(&cc, T, x, nullptr, nullptr, w, x, ffn_ws);
-  fp.a.tiles_r /= pa.fw;
-  fp.a.tiles_s /= pa.fw;
-  fp.b = down_params(&cc, T, nullptr, w, ffn_ws, eout, sout);
-  fp.b.tiles_r /= 2 * pb.fw;
-  fp.b.tiles_s /= 2 * pb.fw;
-  fp.x = x;
-  fp.w_router = w_router;
-  fp.logits_ws = lws;
   fp.d = cc.d_model;
-  fp.expert_out = eout;
-  fp.shared_out = sout;
-  fp.y = y;
+  fp.F = cc.d_ff;
+  fp.ns = cc.num_shared ? 1 : 0;
+  fp.Fs = fp.ns ? cc.d_ff_shared : 0;
+  fp.x = static_cast<const uint16_t*>(x);
+  fp.w_router = static_cast<const uint16_t*>(w_router);
+  fp.logits_ws = lws;
+  fp.w13 = static_cast<const uint16_t*>(w->w13);
+  fp.w2 = static_cast<const uint16_t*>(w->w2);
+  fp.ws13 = fp.ns ? static_cast<const uint16_t*>(w->ws13) : nullptr;
+  fp.ws2 = fp.ns ? static_cast<const uint16_t*>(w->ws2) : nullptr;
+  fp.h = reinterpret_cast<uint16_t*>(b + L.h);
+  fp.y = static_cast<uint16_t*>(y);
   fp.sync = reinterpret_cast<int*>(b + L.sync);
   fp.err = fp.sync + 4;
   fp.spin_limit = kFusedSpinLimit;
-  return hip_status(launch_fused(fp, pa, pb, (hipStream_t)stream));
+  return hip_status(launch_fused(fp, (hipStream_t)stream));
 }
 
 const char* moe_status_string(moe_status status) {

@@ -82,38 +82,40 @@ struct CombineParams {
   int* expert_count;
 };
 
-// The whole layer for a handful of tokens in one persistent launch.  r: the
-// routing rule (r.logits: the layer's logits, or logits_ws when the launch
-// computes them from x and w_router).  a, b: the gate/up and down passes in
-// the compact layout; their offsets come from the launch's own routing and a
-// reads the tokens themselves (no dispatch copy).  sync: four counters, zero
-// between calls (grid barriers after the router GEMM, the gate/up pass and
-// the down pass, then an exit count; the last workgroup out zeroes them).
-// err: set to 1 when a bounded wait gives up (the results are then invalid).
+// The whole layer for a handful of tokens (bf16) in one persistent launch.
+// r: the routing rule (r.logits: the layer's logits, or logits_ws when the
+// launch computes them from x and w_router).  Weights as in moe_weights.  h:
+// the SwiGLU activations handed from the gate/up pass to the down pass, row
+// t*k + j for slot j of token t ([T*k][F]), then the shared expert's row t
+// ([T][Fs]).  sync: counters that are zero between calls (sync[0]: the
+// barrier after the router GEMM, sync[1]: the barrier after the gate/up
+// pass, sync[3]: the exit count; the last workgroup out zeroes them).  err:
+// set to 1 when a bounded wait gives up (the results are then invalid).
 struct FusedParams {
   RouteParams r;
-  FfnParams a, b;
-  const void* x;
-  const void* w_router;  // nullptr: r.logits is an input
+  int d, F, Fs, ns;
+  const uint16_t* x;
+  const uint16_t* w_router;  // nullptr: r.logits is an input
   float* logits_ws;
-  int d;
-  const float* expert_out;
-  const float* shared_out;
-  void* y;
+  const uint16_t* w13;  // [E][2F][d]
+  const uint16_t* w2;   // [E][d][F]
+  const uint16_t* ws13; // [2Fs][d]
+  const uint16_t* ws2;  // [d][Fs]
+  uint16_t* h;
+  uint16_t* y;
   int* sync;
   int* err;
   int spin_limit;
 };
 
-// Launch shape of one pass of the fused layer (four waves): FW column waves
-// x KS reduction splits, activation tiles shared through LDS or not.
-struct FusedPlan {
-  int fw, ks;
-  bool share;
-};
+// Whether the fused launch covers a shape (T tokens, k slots each, E experts,
+// model width d, expert widths F and Fs; Fs = 0 without a shared expert).
+bool fused_shape_ok(int T, int k, int E, int d, int F, int Fs);
+// Workgroups of the fused launch on the current device (one per CU), or 0.
+int fused_grid();
 
 hipError_t launch_route(const RouteParams& p, hipStream_t stream);
-hipError_t launch_fused(const FusedParams& p, const FusedPlan& a, const FusedPlan& b, hipStream_t stream);
+hipError_t launch_fused(const FusedParams& p, hipStream_t stream);
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream);
 // gated: gate/up + SwiGLU pass (output dtype: bf16, or E4M3 with scales for
 // E4M3 weights, or f32); otherwise the down pass (f32 output).  routed_rows

@@ -67,8 +67,9 @@ __device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m)
 // Selection of token t by the calling wave, with no side effects: lane j < k
 // gets the expert of slot j (slots by descending key) in my_idx and its gate
 // weight (routed_scale applied) in my_w.  kbuf holds route_lds_floats(E)
-// floats of this wave's LDS.
-template <int KPL>
+// floats of this wave's LDS.  COHERENT: the logits are read with device-scope
+// loads (they were written earlier in the same launch by other workgroups).
+template <int KPL, bool COHERENT = false>
 __device__ __forceinline__ void route_select(const RouteParams& p, int t, float* kbuf, int& my_idx, float& my_w) {
   const int lane = threadIdx.x & 63;
   const int E = p.E;
@@ -91,7 +92,7 @@ __device__ __forceinline__ void route_select(const RouteParams& p, int t, float*
     const int e = lane * KPL + i;
     float k = -INFINITY, s = 0.f;
     if (e < E) {
-      const float l = lg[e];
+      const float l = COHERENT ? __hip_atomic_load(lg + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lg[e];
       if (p.score_fn == MOE_SCORE_SIGMOID) {
         // sigmoid evaluated in double and rounded once to fp32
         s = (float)(1.0 / (1.0 + exp(-(double)l)));

@@ -24,9 +24,12 @@ template <> struct Piece<MOE_F32> {
   static __device__ __forceinline__ float get(const i32x4_t& v, int i) { return __int_as_float(v[i]); }
 };
 
-// Logits of expert e for all T tokens, by the calling 256-thread workgroup
-// (four waves split d); part holds kGemvWaves x kGemvMaxTokens floats of LDS.
-template <int DT, int PPL>
+// Logits of expert e for all T tokens, by the calling workgroup (waves 0-3
+// split d; any further waves hold no pieces and only meet the barrier); part
+// holds one row of kGemvMaxTokens floats of LDS per wave.  COHERENT: the
+// logits are stored with device-scope stores, for readers elsewhere in the
+// same launch.
+template <int DT, int PPL, bool COHERENT = false>
 __device__ __forceinline__ void router_gemv_body(const uint8_t* __restrict__ x, const uint8_t* __restrict__ w,
                                                  float* logits, int T, int E, int d, int e,
                                                  float (*part)[kGemvMaxTokens]) {
@@ -82,7 +85,10 @@ __device__ __forceinline__ void router_gemv_body(const uint8_t* __restrict__ x, 
     float s = 0.f;
 #pragma unroll
     for (int q = 0; q < kGemvWaves; ++q) s += part[q][threadIdx.x];
-    logits[(size_t)threadIdx.x * E + e] = s;
+    if constexpr (COHERENT)
+      __hip_atomic_store(logits + (size_t)threadIdx.x * E + e, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      logits[(size_t)threadIdx.x * E + e] = s;
   }
 }
 

@@ -252,7 +252,7 @@ moe_status combine_impl(const moe_config* c, int32_t T, const float* eout, const
 
 // ---- the fused decode layer (fused.hip)
 
-constexpr int kFusedSpinLimit = 1 << 22;  // ~0.1 s of s_sleep per grid barrier before giving up
+constexpr int kFusedSpinLimit = 1 << 18;  // polls per grid barrier before giving up (about 0.1-0.3 s)
 
 struct FusedLayout {
   size_t sync, logits, h, total;
@@ -264,14 +264,16 @@ moe_config compact_of(const moe_config* c) {
   return cc;
 }
 
-// sync words (four counters, then the error word) first, so that the zero
-// invariant carries over between calls of any size; then the router's
-// logits [T][E] f32 and h: [T*k][F] bf16 (routed slots), [T][Fs] bf16
-// (shared expert)
+// The words that are zero between calls first (an exit count, the error word,
+// then two 4 KB barrier blocks), so that the zero invariant carries over
+// between calls of any size; then the router's logits [T][E] f32 and h:
+// [T*k][F] bf16 (routed slots), [T][Fs] bf16 (shared expert)
+constexpr size_t kFusedSyncBytes = 3 * kFusedBarWords * sizeof(int);
+
 FusedLayout fused_layout(const moe_config* c, int64_t T) {
   FusedLayout L{};
   size_t o = 0;
-  L.sync = o;   o = align256(o + 8 * sizeof(int));
+  L.sync = o;   o = align256(o + kFusedSyncBytes);
   L.logits = o; o = align256(o + (size_t)T * c->num_experts * sizeof(float));
   L.h = o;      o = align256(o + (size_t)T * c->top_k * c->d_ff * 2 + (c->num_shared ? (size_t)T * c->d_ff_shared * 2 : 0));
   L.total = o;
@@ -572,6 +574,8 @@ moe_status moe_layer_fused(const moe_config* cfg, int32_t T, const void* x, cons
   fp.h = reinterpret_cast<uint16_t*>(b + L.h);
   fp.y = static_cast<uint16_t*>(y);
   fp.sync = reinterpret_cast<int*>(b + L.sync);
+  fp.bar0 = fp.sync + kFusedBarWords;
+  fp.bar1 = fp.sync + 2 * kFusedBarWords;
   fp.err = fp.sync + 4;
   fp.spin_limit = kFusedSpinLimit;
   return hip_status(launch_fused(fp, (hipStream_t)stream));

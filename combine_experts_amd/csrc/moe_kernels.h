@@ -87,10 +87,11 @@ struct CombineParams {
 // launch computes them from x and w_router).  Weights as in moe_weights.  h:
 // the SwiGLU activations handed from the gate/up pass to the down pass, row
 // t*k + j for slot j of token t ([T*k][F]), then the shared expert's row t
-// ([T][Fs]).  sync: counters that are zero between calls (sync[0]: the
-// barrier after the router GEMM, sync[1]: the barrier after the gate/up
-// pass, sync[3]: the exit count; the last workgroup out zeroes them).  err:
-// set to 1 when a bounded wait gives up (the results are then invalid).
+// ([T][Fs]).  Words that are zero between calls (the last workgroup to count
+// out zeroes them): sync[3], the exit count; bar0, bar1: the blocks
+// (kFusedBarWords ints: counters and a release flag) of the barriers after
+// the router GEMM and after the gate/up pass.  err: set to 1 when a bounded wait
+// gives up (the results are then invalid).
 struct FusedParams {
   RouteParams r;
   int d, F, Fs, ns;
@@ -104,9 +105,13 @@ struct FusedParams {
   uint16_t* h;
   uint16_t* y;
   int* sync;
+  int* bar0;
+  int* bar1;
   int* err;
   int spin_limit;
 };
+
+constexpr int kFusedBarWords = 1024;  // ints per barrier block (4 KB)
 
 // Whether the fused launch covers a shape (T tokens, k slots each, E experts,
 // model width d, expert widths F and Fs; Fs = 0 without a shared expert).

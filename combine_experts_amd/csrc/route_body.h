@@ -45,10 +45,10 @@ __host__ __device__ inline int route_lds_floats(int E) { return 2 * E + 384; }
 
 // ---------------------------------------------------------------------------
 // Router: one wavefront per token.  Lane l holds experts l*KPL .. l*KPL+KPL-1.
-// Selection is a radix select on wave ballots (no cross-lane shuffles): the
-// k-th largest selection key is found bit by bit from the top, the experts
-// above it are taken, and ties at it go to the lowest indices.  The chosen k
-// are then put in (key descending, index ascending) order through LDS.
+// Selection takes k rounds of wave-wide argmax (DPP maximum of the lanes'
+// best ordered keys, then the lowest lane holding it): round j picks slot j
+// of the (key descending, index ascending) order directly, so the chosen
+// experts need no separate sort.
 // ---------------------------------------------------------------------------
 
 // Total order of candidates: larger key first, then lower index.
@@ -62,7 +62,19 @@ __device__ __forceinline__ uint32_t ord(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ int popc64(unsigned long long m) { return __popcll(m); }
+// Largest value over the wave, in every lane: DPP row shifts combine each
+// row of 16 lanes into its last lane, row broadcasts carry rows 0 and 2 into
+// rows 1 and 3 and then row 1 into rows 2 and 3, so lane 63 ends with the
+// maximum (lanes without a source take 0, the identity for unsigned max).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 
 // Selection of token t by the calling wave, with no side effects: lane j < k
 // gets the expert of slot j (slots by descending key) in my_idx and its gate
@@ -73,18 +85,26 @@ template <int KPL, bool COHERENT = false>
 __device__ __forceinline__ void route_select(const RouteParams& p, int t, float* kbuf, int& my_idx, float& my_w) {
   const int lane = threadIdx.x & 63;
   const int E = p.E;
-  // per-wave LDS: keys[E], scores[E], group scores[64], group chosen[64],
-  // chosen (key, index) in index order [64 + 64], chosen (index, score) in
-  // output order [64 + 64]
+  // per-wave LDS: keys[E], scores[E], group scores[64], group chosen[64]
   float* sbuf = kbuf + E;
   float* gbuf = sbuf + E;
   float* cbuf = gbuf + 64;
-  uint32_t* cu = reinterpret_cast<uint32_t*>(cbuf + 64);
-  int* ce = reinterpret_cast<int*>(cu + 64);
-  int* oe = ce + 64;
-  float* os = reinterpret_cast<float*>(oe + 64);
 
   const float* lg = p.logits + (size_t)t * E;
+  // every load first (past-the-end lanes read expert 0), so that they are in
+  // flight together
+  float lv[KPL], bv[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane * KPL + i < E ? lane * KPL + i : 0;
+    lv[i] = COHERENT ? __hip_atomic_load(lg + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lg[e];
+  }
+  const bool biased = p.score_fn == MOE_SCORE_SIGMOID && p.bias;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane * KPL + i < E ? lane * KPL + i : 0;
+    bv[i] = biased ? p.bias[e] : 0.f;
+  }
   float key[KPL];
   float lmax = -INFINITY;
 #pragma unroll
@@ -92,11 +112,11 @@ __device__ __forceinline__ void route_select(const RouteParams& p, int t, float*
     const int e = lane * KPL + i;
     float k = -INFINITY, s = 0.f;
     if (e < E) {
-      const float l = COHERENT ? __hip_atomic_load(lg + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lg[e];
+      const float l = lv[i];
       if (p.score_fn == MOE_SCORE_SIGMOID) {
         // sigmoid evaluated in double and rounded once to fp32
         s = (float)(1.0 / (1.0 + exp(-(double)l)));
-        k = p.bias ? s + p.bias[e] : s;
+        k = biased ? s + bv[i] : s;
       } else {
         s = l;
         k = l;
@@ -114,8 +134,36 @@ __device__ __forceinline__ void route_select(const RouteParams& p, int t, float*
   // the topk_group best groups survive
   const int G = p.n_group;
   const int gsize = E / G;
+  const int lpg = gsize / KPL;  // lanes per group when every lane's experts lie in one group
   bool elig[KPL];
-  if (G > 1) {
+  if (G > 1 && gsize % KPL == 0 && (lpg & (lpg - 1)) == 0) {
+    // each group is lpg consecutive lanes: its two largest keys by a
+    // butterfly of (largest, second largest) pairs inside the group, then
+    // each lane ranks its group against every group's score (readlane)
+    float b1 = -INFINITY, b2 = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const float v = key[i];
+      if (v > b1) { b2 = b1; b1 = v; }
+      else if (v > b2) b2 = v;
+    }
+    for (int off = 1; off < lpg; off <<= 1) {
+      const float o1 = __shfl_xor(b1, off), o2 = __shfl_xor(b2, off);
+      const float n1 = fmaxf(b1, o1);
+      b2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+      b1 = n1;
+    }
+    float gs = gsize == 1 ? b1 : b1 + b2;
+    if (gs != gs) gs = -INFINITY;
+    const int myg = lane / lpg;
+    int rank = 0;
+    for (int g = 0; g < G; ++g) {
+      const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs), g * lpg));
+      rank += better(sg, g, gs, myg) ? 1 : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) elig[i] = lane * KPL + i < E && rank < p.topk_group;
+  } else if (G > 1) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     // LPG lanes (a power of two) scan one group together, then merge their
@@ -162,82 +210,48 @@ __device__ __forceinline__ void route_select(const RouteParams& p, int t, float*
     for (int i = 0; i < KPL; ++i) elig[i] = lane * KPL + i < E;
   }
 
-  // ---- top-k: u_t = the k-th largest ordered key among eligible experts,
-  // found bit by bit (count(u >= t) >= k holds for the largest such t)
+  // ---- top-k: k rounds of wave-wide argmax over the eligible experts'
+  // ordered keys.  Ties go to the lowest index (the lowest lane, then the
+  // lowest of its experts), so round j yields slot j of the (key descending,
+  // index ascending) order; the caller's configuration has at least k
+  // eligible experts.
   const int k = p.k;
   uint32_t u[KPL];
 #pragma unroll
-  for (int i = 0; i < KPL; ++i) u[i] = ord(key[i]);
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = thr | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) cnt += popc64(__ballot(elig[i] && u[i] >= c));
-    if (cnt >= k) thr = c;
-  }
-  // everything above the threshold is taken; ties at it by lowest index
-  const unsigned long long below = (1ull << lane) - 1ull;  // lanes with lower experts
-  int n_gt = 0, tie_before = 0;
-  bool gt[KPL], eq[KPL];
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    gt[i] = elig[i] && u[i] > thr;
-    eq[i] = elig[i] && u[i] == thr;
-    n_gt += popc64(__ballot(gt[i]));
-    tie_before += popc64(__ballot(eq[i]) & below);
-  }
-  const int need = k - n_gt;  // >= 1
-  bool sel[KPL];
-  int sel_before = 0;
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    sel[i] = gt[i] || (eq[i] && tie_before < need);
-    tie_before += eq[i] ? 1 : 0;
-  }
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) sel_before += popc64(__ballot(sel[i]) & below);
-  // chosen experts in index order -> LDS
-#pragma unroll
-  for (int i = 0; i < KPL; ++i) {
-    if (sel[i]) {
-      cu[sel_before] = u[i];
-      ce[sel_before] = lane * KPL + i;
-      ++sel_before;
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  // lane j < k places chosen expert j at its rank in (key desc, index asc)
-  if (lane < k) {
-    const uint32_t uj = cu[lane];
-    const int ej = ce[lane];
-    int pos = 0;
-    for (int j = 0; j < k; ++j) {
-      const uint32_t uo = cu[j];
-      pos += (uo > uj || (uo == uj && ce[j] < ej)) ? 1 : 0;
-    }
-    oe[pos] = ej;
-    os[pos] = sbuf[ej];
-  }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  for (int i = 0; i < KPL; ++i) u[i] = elig[i] ? ord(key[i]) : 0u;  // 0: below every ordered key
   my_idx = 0;
-  float my_s = 0.f;
-  if (lane < k) {
-    my_idx = oe[lane];
-    my_s = os[lane];
+  for (int j = 0; j < k; ++j) {
+    uint32_t lb = u[0];
+    int bi = 0;
+#pragma unroll
+    for (int i = 1; i < KPL; ++i)
+      if (u[i] > lb) {
+        lb = u[i];
+        bi = i;
+      }
+    const uint32_t m = wave_max_u32(lb);
+    const int L = __builtin_ctzll(__ballot(lb == m));  // lowest lane holding the maximum
+    const int e = __builtin_amdgcn_readlane(lane * KPL + bi, L);
+    if (lane == L) {
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) u[i] = i == bi ? 0u : u[i];
+    }
+    if (lane == j) my_idx = e;
   }
+  const float my_s = lane < k ? sbuf[my_idx] : 0.f;  // slot j's unbiased score, in lane j
 
   // ---- gate weights from the unbiased scores of the k chosen experts
+  // (slot j's score in lane j, read with readlane: j is uniform), summed in
+  // slot order
+  auto slot_val = [](float v, int j) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j)); };
   float w = 0.f;
   if (p.score_fn == MOE_SCORE_SOFTMAX) {
     if (p.weight_fn == MOE_WEIGHT_NORM_SUM) {
       // p_j / sum p over the chosen = exp(l_j - M) / sum exp(l_i - M); with
       // M the largest chosen logit (the largest logit overall when G = 1)
-      const float m = os[0];
+      const float m = slot_val(my_s, 0);
       float den = 0.f;
-      for (int j = 0; j < k; ++j) den += expf(os[j] - m);
+      for (int j = 0; j < k; ++j) den += expf(slot_val(my_s, j) - m);
       w = expf(my_s - m) / den;
     } else {
       // p_e = exp(l_e - M) / Z over all experts
@@ -254,21 +268,21 @@ __device__ __forceinline__ void route_select(const RouteParams& p, int t, float*
       for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
       const float pj = expf(my_s - m) / z;
       float pm = -INFINITY;
-      for (int j = 0; j < k; ++j) pm = fmaxf(pm, __shfl(pj, j));
+      for (int j = 0; j < k; ++j) pm = fmaxf(pm, slot_val(pj, j));
       float den = 0.f;
-      for (int j = 0; j < k; ++j) den += expf(__shfl(pj, j) - pm);
+      for (int j = 0; j < k; ++j) den += expf(slot_val(pj, j) - pm);
       w = expf(pj - pm) / den;
     }
   } else {
     if (p.weight_fn == MOE_WEIGHT_NORM_SUM) {
       float den = 0.f;
-      for (int j = 0; j < k; ++j) den += os[j];
+      for (int j = 0; j < k; ++j) den += slot_val(my_s, j);
       w = my_s / den;
     } else {
       float sm = -INFINITY;
-      for (int j = 0; j < k; ++j) sm = fmaxf(sm, os[j]);
+      for (int j = 0; j < k; ++j) sm = fmaxf(sm, slot_val(my_s, j));
       float den = 0.f;
-      for (int j = 0; j < k; ++j) den += expf(os[j] - sm);
+      for (int j = 0; j < k; ++j) den += expf(slot_val(my_s, j) - sm);
       w = expf(my_s - sm) / den;
     }
   }

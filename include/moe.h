@@ -310,16 +310,20 @@ moe_status moe_layer(const moe_config* cfg, int32_t T, const void* x, const floa
  *   logits are computed in the launch, with moe_router_logits' arithmetic.
  *   x, bias, w, y: as for moe_layer.  masked_layout is ignored.
  *   ws, ws_bytes: workspace of at least moe_fused_workspace_size(cfg, T)
- *   bytes, zero-filled once by the caller; the launch leaves its counters at
- *   zero, so the same workspace serves every later call.  The int at byte 16
- *   of ws is set to 1 (and never cleared by the library) when one of the
- *   launch's bounded grid-wide waits gave up: the results of that call are
- *   then invalid.
+ *   bytes, zero-filled once by the caller.  Its first 12 KB hold the grid
+ *   barriers' counters and flags, which the launch leaves at zero, so the
+ *   same workspace serves every later call; the rest is scratch the launch
+ *   writes before it reads.  The int at byte 16 of ws is set to 1 (and never
+ *   cleared by the library) when one of the launch's bounded grid-wide waits
+ *   gave up (for instance on counters that were not zero): the results of
+ *   that call are then invalid.
  *   Supported (else MOE_ERR_UNSUPPORTED, nothing launched): bf16 activations
- *   and weights, 1 <= T <= 16, T*k <= 256, E <= 256, d <= 16384 when w_router
- *   is given (moe_fused_supported tells).  Routing, weights and rows follow
- *   moe_layer exactly; an expert's rows are ordered by token (no atomics),
- *   so the output is reproducible bit for bit run to run.
+ *   and weights, 1 <= T <= 16, T*k <= 256, E <= 256, d, d_ff and d_ff_shared
+ *   multiples of 128, d <= 16384 when w_router is given (moe_fused_supported
+ *   tells).  Routing and weights follow moe_layer exactly; each token's
+ *   expert outputs are added in a fixed order (ascending expert, then the
+ *   shared expert) with no atomics, so the output is reproducible bit for
+ *   bit run to run.
  *   The launch keeps one workgroup on every CU and synchronises them with
  *   grid-wide barriers: it must not share the GPU with another launch that
  *   occupies every CU for long (it waits for CUs, within its bound).

@@ -144,7 +144,7 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // Grid-wide barrier of the resident workgroups, two levels deep.  The waves
 // that stored data for other workgroups (all of them, or with all_store
-// false only the epilogue wave, the others keeping their loads in flight)
+// false only the epilogue wave)
 // first wait until their own (device-scope) stores are done; then the
 // epilogue wave's first lane counts the workgroup in on its group's counter
 // (workgroup b is in group b % 8, the counters 256 bytes apart), the last
@@ -182,6 +182,10 @@ __device__ __forceinline__ void grid_sync(int* bar, int nblk, int* err, int spin
 }
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Relative cost of one gate/up unit whose group has n token columns: 16 weight
+// rows plus n token columns at 3/4 of a row each, in quarters of a row.
+__device__ __forceinline__ int unit_cost(int n) { return 64 + 3 * n; }
 
 __device__ __forceinline__ uint32_t mix(uint32_t v) { return (v * 2654435761u) >> 16; }
 
@@ -256,12 +260,14 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
   constexpr int RB = (DA * BST > DB * BSTP ? DA * BST : DB * BSTP) * kStream;
   __shared__ __attribute__((aligned(16))) uint8_t ringA[DA * kStream * kAWin];
   __shared__ __attribute__((aligned(16))) uint8_t ringB[RB];
-  // partial sums: gate/up [2 units in flight][4 waves][4][64]; down [4 waves][2 tiles][4][64]
-  __shared__ float red[2 * kStream * 4 * 64];
+  // partial sums: gate/up [2 units in flight][4 waves][64 lanes][4]; down [4 waves][2 tiles][64][4]
+  __shared__ __attribute__((aligned(16))) float red[2 * kStream * 4 * 64];
   __shared__ int s_idx[kMaxSlots];
   __shared__ float s_w[kMaxSlots];
   __shared__ int s_mark[kMaxE];
   __shared__ int s_grp[kMaxE];
+  __shared__ int s_gcost[kMaxE + 1];  // cost of group g's gate/up units
+  __shared__ int s_gpre[kMaxE + 1];   // cost of the groups before g
   __shared__ int s_meta[4];
   __shared__ float s_part[kWaves][kGemvMaxTokens];
 
@@ -302,9 +308,12 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
     }
   }
   __syncthreads();
+  const int n8r = F / 8, n8s = ns ? Fs / 8 : 0;  // gate/up units (8 columns of h) per group
   if (wid == 0) {
-    // one wave: mark the chosen experts, then list them in index order
-    for (int i = lane; i < T * k; i += 64) s_mark[s_idx[i]] = 1;
+    // one wave: count each expert's tokens (a token picks an expert at most
+    // once), list the experts with tokens in index order, and the prefix of
+    // the groups' gate/up cost (see below)
+    for (int i = lane; i < T * k; i += 64) atomicAdd(&s_mark[s_idx[i]], 1);
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     int c = 0;
@@ -317,12 +326,45 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
       if (lane >= o) inc += y;
     }
     int pos = inc - c;
+    const int gr = __shfl(inc, 63);
 #pragma unroll
     for (int i = 0; i < kKpl; ++i) {
       const int e = lane * kKpl + i;
-      if (e < E && s_mark[e]) s_grp[pos++] = e;
+      if (e < E && s_mark[e]) {
+        s_grp[pos] = e;
+        s_gcost[pos] = n8r * unit_cost(s_mark[e]);
+        ++pos;
+      }
     }
-    if (lane == 63) s_meta[0] = inc;
+    if (lane == 0 && ns) s_gcost[gr] = n8s * unit_cost(T);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // exclusive prefix of the group costs over the gr + ns groups (<= 257)
+    const int ng = gr + (ns ? 1 : 0);
+    int v[5], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int g = lane * 5 + i;
+      v[i] = g < ng ? s_gcost[g] : 0;
+      sum += v[i];
+    }
+    int inc2 = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc2, o);
+      if (lane >= o) inc2 += y;
+    }
+    int run = inc2 - sum;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      const int g = lane * 5 + i;
+      if (g < ng) s_gpre[g] = run;
+      run += v[i];
+    }
+    if (lane == 63) {
+      s_meta[0] = gr;
+      s_meta[1] = inc2;  // total cost
+    }
   }
   __syncthreads();
   const int Gr = uni(s_meta[0]);    // routed experts with tokens
@@ -352,7 +394,11 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
   // column c; the MFMA B operand of lane (lg, r16) for piece q of step j is
   // slot ((j 4 + q) 4 + lg) TP + r16.  The loads fill the slots densely, 64
   // per instruction (slot 64 i + lane), so a stage of TP columns and NB steps
-  // takes 16 TP NB / 64 load instructions rather than 4 per step.
+  // takes 16 TP NB / 64 load instructions rather than 4 per step.  Only the
+  // columns of the group's own tokens are loaded; every instruction covers all
+  // TP columns and every group has a token, so each instruction still issues
+  // (the wait counts above count instructions).  The other columns keep stale
+  // LDS: their products are never used.
   const int bc = lane % TP;  // token column of every slot this lane loads
   auto tile_off = [&](int i) {
     const int sl = 64 * i + lane, j = sl / (16 * TP), q = (sl / (4 * TP)) % 4, g = (sl / TP) % 4;
@@ -366,10 +412,28 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
   // where this lane's MFMA B operand sits in a step's token tile
   const int bslot = (lg * TP + (r16 < TP ? r16 : 0)) * 16;
 
-  // ---- 2. gate/up + SwiGLU over this workgroup's units
-  const int n8r = F / 8, n8s = ns ? Fs / 8 : 0;
+  // ---- 2. gate/up + SwiGLU over this workgroup's units.  A unit of a group
+  // with n tokens streams 16 weight rows and n token columns per K-step; the
+  // units are split over the grid in contiguous runs of equal total cost
+  // unit_cost(n) (measured: a token column costs about 3/4 of a weight row
+  // per step), so that groups with many tokens (the shared expert) do not
+  // leave their workgroups behind.  Workgroup b takes the units whose start
+  // (the cost of the units before them) lies in [b C / nblk, (b+1) C / nblk).
   const long long U = (long long)Gr * n8r + n8s;
-  const int ua = (int)(U * bid / nblk), ub = (int)(U * (bid + 1) / nblk);
+  const long long Ctot = uni(s_meta[1]);
+  auto first_unit = [&](long long X) -> int {  // first unit starting at or after cost X
+    if (X >= Ctot) return (int)U;
+    int ng = 0;  // groups starting at or before X
+    for (int i = 0; i < 5; ++i) {
+      const int g = lane * 5 + i;
+      ng += __popcll(__ballot(g < G && s_gpre[g] <= X));
+    }
+    const int g = ng - 1;
+    const int cg = unit_cost(g < Gr ? uni(s_mark[uni(s_grp[g])]) : T);
+    const long long before = (X - uni(s_gpre[g]) + cg - 1) / cg;  // units of g that start before X
+    return (int)((long long)g * n8r + before);
+  };
+  const int ua = first_unit(Ctot * bid / nblk), ub = first_unit(Ctot * (bid + 1) / nblk);
   const int nunits = ub - ua;
   const int SA = d / 128;  // K-steps of a unit
   // unit u -> group g (Gr: the shared expert), first h column f0
@@ -391,9 +455,11 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
     const uint8_t* xrow = reinterpret_cast<const uint8_t*>(fp.x) + (size_t)(bc < T ? bc : 0) * dB;
     int iu = 0, ij = 0, irot = 0, islot = 0;
     const uint8_t* arow = nullptr;
+    bool bon = false;  // this lane's token column is one of the unit's tokens (others are not loaded)
     auto set_unit = [&](int u) {
       int g, f0;
       unit_of(ua + u, g, f0);
+      bon = hrow_of(bc, g) >= 0;
       const int Fg = g < Gr ? F : Fs;
       const uint8_t* base = g < Gr ? w13 + (size_t)s_grp[g] * 2 * F * dB : ws13;
       const int row = r16 < 8 ? f0 + r16 : Fg + f0 + r16 - 8;
@@ -411,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
       uint8_t* wb = ringB + (islot * kStream + wid) * BST;
 #pragma unroll
       for (int i = 0; i < NBA; ++i)
-        if (64 * i + lane < 16 * TP) dma16<0>(xrow + off + boA[i], wb + 1024 * i);
+        if (64 * i + lane < 16 * TP && bon) dma16<0>(xrow + off + boA[i], wb + 1024 * i);
       islot = islot + 1 == DA ? 0 : islot + 1;
       if (++ij == nw) {
         ij = 0;
@@ -433,9 +499,8 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
       cslot = cslot + 1 == DA ? 0 : cslot + 1;
       if (++cj == nw) {  // end of this wave's share of a unit
         cj = 0;
-        float* dst = red + ((par * kStream + wid) * 4) * 64 + lane;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[r * 64] = cnt > 0 ? acc[r] : 0.f;
+        *reinterpret_cast<f32x4_t*>(red + ((par * kStream + wid) * 64 + lane) * 4) =
+            cnt > 0 ? acc : f32x4_t{0.f, 0.f, 0.f, 0.f};
         acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
         par ^= 1;
         lds_barrier();  // the unit's partial sums are in LDS
@@ -446,44 +511,44 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
     // epilogue wave: partial sums -> SwiGLU -> h, one unit per barrier.  Lane
     // l < 32 holds gate rows 4 lg .. 4 lg + 3 of token column r16 (the up
     // rows are the same offsets in lanes l + 32): h columns f0 + 4 lg .. +3.
+    // The unit's h row is looked up before its barrier, off the critical path.
     for (int u = 0; u < nunits; ++u) {
-      lds_barrier();
+      int g, f0, row = -1;
       if (lane < 32) {
-        int g, f0;
         unit_of(ua + u, g, f0);
-        const int row = hrow_of(r16, g);
-        if (row >= 0) {
-          const float* src = red + ((u & 1) * kStream * 4) * 64 + lane;
-          uint32_t packed[2];
+        row = hrow_of(r16, g);
+      }
+      lds_barrier();
+      if (row >= 0) {
+        const float* src = red + ((u & 1) * kStream * 64 + lane) * 4;
+        f32x4_t gs = {0.f, 0.f, 0.f, 0.f}, us = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; r += 2) {
-            float hv[2];
+        for (int w = 0; w < kStream; ++w) {
+          const f32x4_t gw = *reinterpret_cast<const f32x4_t*>(src + w * 256);
+          const f32x4_t uw = *reinterpret_cast<const f32x4_t*>(src + w * 256 + 128);
 #pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-              float gs = 0.f, us = 0.f;
-#pragma unroll
-              for (int w = 0; w < kStream; ++w) {
-                gs += src[(w * 4 + r + e2) * 64];
-                us += src[(w * 4 + r + e2) * 64 + 32];
-              }
-              hv[e2] = silu(gs) * us;
-            }
-            packed[r / 2] = f32_to_bf16_bits(hv[0]) | (f32_to_bf16_bits(hv[1]) << 16);
+          for (int r = 0; r < 4; ++r) {
+            gs[r] += gw[r];
+            us[r] += uw[r];
           }
-          uint8_t* dst = g < Gr ? hr + (size_t)row * F * 2 : hs + (size_t)row * Fs * 2;
-          const uint64_t v = (uint64_t)packed[0] | ((uint64_t)packed[1] << 32);
-          __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + (size_t)(f0 + 4 * lg) * 2), v, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
         }
+        uint32_t packed[2];
+#pragma unroll
+        for (int r = 0; r < 4; r += 2)
+          packed[r / 2] = f32_to_bf16_bits(silu(gs[r]) * us[r]) | (f32_to_bf16_bits(silu(gs[r + 1]) * us[r + 1]) << 16);
+        uint8_t* dst = g < Gr ? hr + (size_t)row * F * 2 : hs + (size_t)row * Fs * 2;
+        const uint64_t v = (uint64_t)packed[0] | ((uint64_t)packed[1] << 32);
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(dst + (size_t)(f0 + 4 * lg) * 2), v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
 
   // ---- 3. every h of the layer is written; 4. down + combine over this
   // workgroup's columns [wlo, whi) of y, in chunks of at most CHR columns.
-  // The first chunk's weight tiles do not depend on h: the streaming waves
-  // issue its first DB stages' weight loads before the barrier and only the
-  // token (h) loads after it.
+  // (Issuing the first weight tiles of the down pass before the barrier was
+  // measured no faster: the burst of loads delays the barrier's atomics by
+  // about as much as it saves in the down pass.)
   constexpr int RT = 16 / P;            // y columns per tile
   constexpr int CHR = P == 1 ? 16 * kMaxTiles : RT;
   const int Q = d / 4;
@@ -517,8 +582,8 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
     arow = (sh ? ws2 : w2 + (size_t)e * d * F * 2) + (size_t)row * Fg * 2 + 16 * lg + (P == 2 && r16 >= 8 ? 256 : 0);
     if (ic.g != hgroup) {
       hgroup = ic.g;
-      const int r = hrow_of(bc, ic.g);  // columns of no token read row 0
-      hrow = r < 0 ? hr : sh ? hs + (size_t)r * Fs * 2 : hr + (size_t)r * F * 2;
+      const int r = hrow_of(bc, ic.g);  // columns of none of the group's tokens are not loaded
+      hrow = r < 0 ? nullptr : sh ? hs + (size_t)r * Fs * 2 : hr + (size_t)r * F * 2;
     }
     rot = (int)(mix((uint32_t)((sh ? kMaxE : e) * 4096 + lo / 16 + ic.tile)) % (uint32_t)ic.S);
   };
@@ -553,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
   auto stage_src = [&](const uint8_t*& asrc, const uint8_t*& bsrc) {
     const int ps = ic.s + rot < ic.S ? ic.s + rot : ic.s + rot - ic.S;
     asrc = arow + (size_t)(P * ps) * 256;
-    bsrc = hrow + (size_t)(P * ps) * 256;
+    bsrc = hrow ? hrow + (size_t)(P * ps) * 256 : nullptr;
     if (advance(ic) && ic.g < G) set_seg();
   };
   auto dmaA = [&](int slot, const uint8_t* asrc) {
@@ -565,23 +630,9 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
     uint8_t* wb = ringB + (slot * kStream + wid) * BSTP;
 #pragma unroll
     for (int i = 0; i < NBB; ++i)
-      if (64 * i + lane < 16 * P * TP) dma16<kSc1>(bsrc + boB[i], wb + 1024 * i);
+      if (64 * i + lane < 16 * P * TP && bsrc) dma16<kSc1>(bsrc + boB[i], wb + 1024 * i);
   };
-  constexpr int NB = NBB, NS = NSB;  // token loads, all loads of a stage
-  const uint8_t* bpre[DB];
-  int npre = 0;  // stages whose token loads wait for the barrier
-  if (wid < kStream && lo < whi) {
-    setup_chunk();
-    npre = min(n, DB);
-#pragma unroll
-    for (int i = 0; i < DB; ++i) {
-      if (i < npre) {
-        const uint8_t* asrc;
-        stage_src(asrc, bpre[i]);
-        dmaA(i, asrc);
-      }
-    }
-  }
+  constexpr int NS = NSB;  // loads of a stage
 
   grid_sync(fp.bar1, nblk, fp.err, fp.spin_limit, false);
   // count this workgroup out of the barriers now; the answer is needed only
@@ -589,24 +640,17 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
   int exit_rank = 0;
   if (tid == 64 * kEpi) exit_rank = __hip_atomic_fetch_add(fp.sync + 3, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  for (bool first = true; lo < whi; lo += CHR, hi = min(whi, lo + CHR), first = false) {  // uniform
+  for (; lo < whi; lo += CHR, hi = min(whi, lo + CHR)) {  // uniform
     nt = (hi - lo + RT - 1) / RT;
     if (wid < kStream) {
       f32x4_t y0 = {0.f, 0.f, 0.f, 0.f}, y1 = {0.f, 0.f, 0.f, 0.f};
-      if (first) {
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-          if (i < npre) dmaB(i, bpre[i]);
-      } else {
-        setup_chunk();
-        npre = 0;
-        for (int i = 0; i < min(n, DB); ++i) {
-          const uint8_t* asrc;
-          const uint8_t* bsrc;
-          stage_src(asrc, bsrc);
-          dmaA(i, asrc);
-          dmaB(i, bsrc);
-        }
+      setup_chunk();
+      for (int i = 0; i < min(n, DB); ++i) {  // stage i in slot i
+        const uint8_t* asrc;
+        const uint8_t* bsrc;
+        stage_src(asrc, bsrc);
+        dmaA(i, asrc);
+        dmaB(i, bsrc);
       }
       if (n > 0) {
         // this lane's token column in the consume cursor's group: taken, gate weight
@@ -620,9 +664,7 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
         set_fold();
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
         for (int p = 0; p < n; ++p) {
-          // loads issued after this stage's last one
-          const int m = p < npre ? NB * (npre - 1 - p) + NS * max(0, min(n, DB + p) - DB)
-                                 : NS * min(DB - 1, n - 1 - p);
+          const int m = NS * min(DB - 1, n - 1 - p);  // loads issued after this stage's last one
           i32x4_t a[4], b[4 * P];
           stage_read<P>(m / 4, la + (cslot * kStream + wid) * kAWin + lane * 16,
                         lb + (cslot * kStream + wid) * BSTP + bslot, BWIN, a, b);
@@ -672,12 +714,8 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
           }
         }
       }
-      float* dst = red + (wid * kMaxTiles * 4) * 64 + lane;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        dst[r * 64] = y0[r];
-        dst[(4 + r) * 64] = y1[r];
-      }
+      *reinterpret_cast<f32x4_t*>(red + ((wid * kMaxTiles + 0) * 64 + lane) * 4) = y0;
+      *reinterpret_cast<f32x4_t*>(red + ((wid * kMaxTiles + 1) * 64 + lane) * 4) = y1;
     }
     lds_barrier();
     if (wid == kEpi) {
@@ -685,13 +723,12 @@ __global__ __launch_bounds__(kThreads) void fused_layer_kernel(FusedParams fp) {
       for (int t = 0; t < nt; ++t) {
         const int row = lo + RT * t + 4 * lg;
         if (r16 < T && row < hi && 4 * lg < RT) {
-          float v[4];
+          f32x4_t v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float sum = 0.f;
+          for (int w = 0; w < kStream; ++w) {
+            const f32x4_t pw = *reinterpret_cast<const f32x4_t*>(red + ((w * kMaxTiles + t) * 64 + lane) * 4);
 #pragma unroll
-            for (int w = 0; w < kStream; ++w) sum += red[((w * kMaxTiles + t) * 4 + r) * 64 + lane];
-            v[r] = sum;
+            for (int r = 0; r < 4; ++r) v[r] += pw[r];
           }
           const uint32_t lo2 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
           const uint32_t hi2 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);

@@ -149,7 +149,7 @@ def _touched(wl, inp):
 SMALL_LAYER = [("tiny", 16), ("tiny", 1), ("tiny", 17), ("tiny", 129), ("qwen3", 1), ("qwen3", 8),
                ("qwen3", 32), ("qwen3", 128), ("qwen3", 3), ("k1_groups", 33), ("softmax_sel", 50),
                ("fp8_small", 1), ("fp8_small", 37), ("f32_shared", 40), ("tiled_small", 300),
-               ("tiled_small", 129), ("tiled_narrow", 257), ("qwen3", 512),
+               ("tiled_small", 129), ("tiled_small", 1100), ("tiled_narrow", 257), ("qwen3", 512),
                ("fp8_rows", 200), ("fp8_rows", 67), ("cosched", 1), ("cosched", 45),
                ("share_odd", 40), ("fp8_odd", 3), ("fp8_odd", 40)]
 

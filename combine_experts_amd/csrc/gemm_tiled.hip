@@ -239,23 +239,38 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
   const int g4 = lane >> 4, r16 = lane & 15;
 
   f32x4_t acc[4][4];
+  // Both 32-wide sub-steps' operands are read up front.  The schedule (group
+  // barriers below): the first sub-step's eight reads, then the step's
+  // direct-to-LDS loads, then its MFMAs with the second sub-step's reads
+  // slotted between them, then the rest; so the MFMA pipe waits for LDS only
+  // once per step, right after the barrier.
   auto compute = [&](const uint8_t* wb, const uint8_t* tb) {
+    bf16x8_t av[2][4], bv[2][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int ch = 4 * ks + g4;
-      bf16x8_t av[4], bv[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
-        av[nb] = *reinterpret_cast<const bf16x8_t*>(wb + swz(arow[nb] + r16, ch));
+        av[ks][nb] = *reinterpret_cast<const bf16x8_t*>(wb + swz(arow[nb] + r16, ch));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
-        bv[mb] = *reinterpret_cast<const bf16x8_t*>(tb + swz(brow0 + 16 * mb + r16, ch));
+        bv[ks][mb] = *reinterpret_cast<const bf16x8_t*>(tb + swz(brow0 + 16 * mb + r16, ch));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[nb], bv[mb], acc[nb][mb], 0, 0, 0);
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks][nb], bv[ks][mb], acc[nb][mb], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x020, P, 0);  // direct-to-LDS loads
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 24, 0);
   };
 
   auto epilogue = [&](const TItem& it) {

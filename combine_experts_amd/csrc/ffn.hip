@@ -187,7 +187,13 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
   q.tiles_r = p.tiles_r / per_item;
   q.tiles_s = p.tiles_s / per_item;
   if (q.tiles_r * per_item != p.tiles_r || q.tiles_s * per_item != p.tiles_s) return hipErrorInvalidValue;
-  const int CH = wide ? 32 : 16;
+  // Those batches take 64-row chunks where the launch shape allows (the
+  // gated pass, and the down pass without a K-split): a group of 33-64 rows
+  // then streams its weight tiles once instead of twice.  Measured at 512
+  // tokens x 8 of 256 experts against 32-row chunks: gate/up 1280 -> 1195 us,
+  // down 666 -> 629 us, layer 2072 -> 1936 us.
+  const bool wide64 = wide && (gated || (pl.ks == 1 && (pl.fw == 8 || pl.fw == 4)));
+  const int CH = wide64 ? 64 : wide ? 32 : 16;
   // CH-row chunks over all groups: full chunks plus at most one partial
   // chunk per group (bounds the items, which sizes the grid)
   const long long chunks_r = routed_rows / CH + max_groups;
@@ -219,6 +225,11 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
     }
     if (gated) return launch_plan<MOE_BF16, true, MOE_BF16>(q, pl, items, stream);
     return launch_plan<MOE_BF16, false, MOE_F32>(q, pl, items, stream);
+  }
+  if (wide64) {
+    if (gated) return launch_one<MOE_FP8_E4M3, 8, 1, 4, true, MOE_FP8_E4M3, 2, false, true>(q, items, stream);
+    if (pl.fw == 8) return launch_one<MOE_FP8_E4M3, 8, 1, 4, false, MOE_F32, 2, false, true>(q, items, stream);
+    return launch_one<MOE_FP8_E4M3, 4, 1, 4, false, MOE_F32, 2, false, true>(q, items, stream);
   }
   if (wide) {
     // The waves of a workgroup share each step's 32-row activation tile

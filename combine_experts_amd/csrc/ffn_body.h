@@ -361,6 +361,25 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk, 
   };
   auto compute = [&](const St& s, const Cursor& c, int slot) {
     const int left = c.it.nrows;  // rows of this item (> 0)
+    if constexpr (FP8 && SHARE && TT > 2) {
+      // 64-row chunks: one token block's operand at a time, read from the
+      // LDS slot just before its MFMAs (holding all four would not fit)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        if (tt * 16 < left) {
+          const Step xv = xstep(s, slot, tt);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) {
+            const f32x4_t p0 = mma_fp8_block(s.w[m], xv, 0);
+            const f32x4_t p1 = mma_fp8_block(s.w[m], xv, 1);
+            const float c0 = s.sw[m][0] * s.sx[0][tt][0], c1 = s.sw[m][1] * s.sx[0][tt][1];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[m][tt][j] += p0[j] * c0 + p1[j] * c1;
+          }
+        }
+      }
+      return;
+    }
     Step xb[TT];
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)

@@ -53,10 +53,7 @@ __global__ __launch_bounds__(64 * FW * KS) void ffn_kernel(FfnParams p) {
 // is an unused dynamic LDS reservation sized so a second workgroup cannot
 // fit.  The E4M3 walks stay at full occupancy: their dequantising down pass
 // measured no better under the cap.
-#ifndef MOE_FFN_RESIDENT
-#define MOE_FFN_RESIDENT 1
-#endif
-static constexpr int kResidentCap = MOE_FFN_RESIDENT;
+static constexpr int kResidentCap = 1;
 
 template <int DT, int FW, int KS, int TT, bool GATED, int OUT, int NM = 2, bool PARK = true, bool SHARE = false>
 static hipError_t launch_one(const FfnParams& p, long long max_items, hipStream_t stream) {
@@ -91,8 +88,7 @@ static hipError_t launch_one(const FfnParams& p, long long max_items, hipStream_
 
 // Launch shape of a pass: FW column tiles x KS reduction splits per
 // workgroup, 16-row token tiles (one per item).  KS must not exceed the K-steps of any
-// item (every wave needs at least one step per item).  The MOE_FFN_* macros
-// pin a shape for launch-shape sweeps.
+// item (every wave needs at least one step per item).
 struct Plan {
   int fw, ks;
 };
@@ -106,12 +102,6 @@ static Plan plan_of(const FfnParams& p, int step, bool gated, int wdtype) {
   if (steps < 32) pl = steps >= 8 ? Plan{2, 2} : Plan{gated ? 4 : 2, 1};
   if (steps < pl.ks) pl = Plan{gated ? 4 : 2, 1};
   if (gated && wdtype == MOE_FP8_E4M3) pl = Plan{8, 1};
-#ifdef MOE_FFN_FW
-  if (!(gated && wdtype == MOE_FP8_E4M3)) pl.fw = MOE_FFN_FW;
-#endif
-#ifdef MOE_FFN_KS
-  if (!(gated && wdtype == MOE_FP8_E4M3)) pl.ks = MOE_FFN_KS < steps ? MOE_FFN_KS : steps;
-#endif
   return pl;
 }
 
@@ -143,7 +133,6 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
   // leave no registers for parked accumulators, so those walks finish each
   // item in line.
   const bool wide = wdtype == MOE_FP8_E4M3 && routed_rows >= 12LL * max_groups;
-#ifndef MOE_FFN_FW
   // Once experts hold a few rows each, the E4M3 down pass does better with
   // more column waves sharing each activation tile and no K-split.  Measured
   // at 256 experts x 8 slots, down pass with (2, 2) / (4, 1) / (8, 1): 512
@@ -180,7 +169,6 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
     if (p.n_shared && p.K_s / step < st) st = p.K_s / step;
     if (st < 16 && p.tiles_r % 8 == 0 && p.tiles_s % 8 == 0) pl = Plan{4, 1};
   }
-#endif
   // a work item covers FW waves' columns; a plain-pass wave covers two tiles
   const int per_item = pl.fw * (gated ? 1 : 2);
   FfnParams q = p;
@@ -214,11 +202,7 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
     // under the (4, 1) shape chosen above.
     int steps = q.K_r / step;
     if (q.n_shared && q.K_s / step < steps) steps = q.K_s / step;
-#ifndef MOE_FFN_FW
     const bool dense4 = dense_plain && pl.fw == 4 && pl.ks == 1;
-#else
-    const bool dense4 = false;
-#endif
     if ((pl.fw >= 2 && steps >= 16 && even) || dense4) {
       if (gated) return launch_plan<MOE_BF16, true, MOE_BF16, 1, true, true>(q, pl, items, stream);
       return launch_plan<MOE_BF16, false, MOE_F32, 1, true, true>(q, pl, items, stream);

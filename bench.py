@@ -498,9 +498,10 @@ def kernel_traffic(key, source):
 
 def uses_tiled(wl, T):
     """The library's choice of grouped-GEMM kernel: the LDS-tiled one for
-    bf16 batches with 32 or more rows per expert on average, else the
-    weight-streaming one."""
-    return wl.weight_dtype == "bf16" and T * wl.top_k >= 32 * wl.num_experts
+    bf16 batches with at least 5 (d_model >= 6144), 8 (d_model >= 3072) or
+    12 rows per expert on average, else the weight-streaming one."""
+    r = 5 if wl.d_model >= 6144 else 8 if wl.d_model >= 3072 else 12
+    return wl.weight_dtype == "bf16" and T * wl.top_k >= r * wl.num_experts
 
 
 def main():

@@ -204,11 +204,20 @@ int max_groups_of(const moe_config* c, int32_t T) {
 
 // no expert takes a token twice and the shared expert takes all T, so no
 // group has more than T rows
-// Prefill-sized batches (on average 32 or more rows per expert) take the
-// LDS-tiled bf16 kernel, which reuses each weight tile across 128 token rows;
-// decode-sized ones take the weight-streaming kernel.
+// Batches with enough rows per expert take the LDS-tiled bf16 kernel, which
+// streams each weight tile once per 128 token rows; smaller ones take the
+// weight-streaming kernel, which streams it once per 16-row chunk.  The
+// crossover falls with the row length (the tiled kernel's per-item cost is
+// spread over more K-steps), measured as whole-layer A/B runs:
+//   d_model 7168 (256 experts, top 8): 4 rows per expert (128 tokens)
+//     streaming 2809 / tiled 2850 us; 5 rows 2973 / 2861; 6 rows 3232 / 2919;
+//     12 rows 4532 / 3157; 24 rows 7289 / 3528;
+//   d_model 2048 (128 experts, top 8): 8 rows 231 / 250 us; 10 rows 236 /
+//     250; 12 rows 256 / 256; 14 rows 272 / 257; 16 rows 308 / 261.
 bool use_tiled(const moe_config* c, int32_t T) {
-  return c->weight_dtype == MOE_BF16 && (int64_t)T * c->top_k >= 32LL * c->num_experts;
+  if (c->weight_dtype != MOE_BF16) return false;
+  const int rows_per_expert = c->d_model >= 6144 ? 5 : c->d_model >= 3072 ? 8 : 12;
+  return (int64_t)T * c->top_k >= (int64_t)rows_per_expert * c->num_experts;
 }
 
 // bound on the 128-row token tiles over all routed groups

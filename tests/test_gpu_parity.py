@@ -150,7 +150,8 @@ SMALL_LAYER = [("tiny", 16), ("tiny", 1), ("tiny", 17), ("tiny", 129), ("qwen3",
                ("qwen3", 32), ("qwen3", 128), ("qwen3", 3), ("k1_groups", 33), ("softmax_sel", 50),
                ("fp8_small", 1), ("fp8_small", 37), ("f32_shared", 40), ("tiled_small", 300),
                ("tiled_small", 129), ("tiled_small", 1100), ("tiled_narrow", 257), ("qwen3", 512),
-               ("fp8_rows", 200), ("fp8_rows", 67), ("cosched", 1), ("cosched", 45),
+               ("fp8_rows", 200), ("fp8_rows", 67), ("cosched", 1), ("cosched", 45), ("cosched", 60),
+               ("qwen3", 256),
                ("share_odd", 40), ("fp8_odd", 3), ("fp8_odd", 40)]
 
 
@@ -209,8 +210,9 @@ def test_moe_layer_equals_chain_and_reuses_workspace(name, Ts):
 # Full-size workloads: everything at full size, outputs on sampled tokens
 # ---------------------------------------------------------------------------
 
-BIG_LAYER = [("dsv3", 1), ("dsv3", 8), ("dsv3", 32), ("dsv3", 128), ("dsv3_fp8", 32), ("dsv3_fp8", 128),
-             ("dsv3_fp8", 512), ("dsv3_prefill", 4096)]
+# dsv3 at 192 tokens: 6 rows per expert, which takes the LDS-tiled kernel at this d_model
+BIG_LAYER = [("dsv3", 1), ("dsv3", 8), ("dsv3", 32), ("dsv3", 128), ("dsv3", 192), ("dsv3_fp8", 32),
+             ("dsv3_fp8", 128), ("dsv3_fp8", 512), ("dsv3_prefill", 4096)]
 
 
 @pytest.mark.timeout(900)

@@ -589,6 +589,7 @@ def main():
             ent = {
                 "workload": WORKLOAD_NAMES[name], "tokens": T, "layout": "masked" if layer.masked else "compact",
                 "launch": "hip graph replay" if args.graph else "direct", "touched_experts": D,
+                "grouped_gemm": "lds_tiled" if uses_tiled(b_wl, T) else "weight_streaming",
                 "layer_us_median": round(med, 2), "layer_us_p10": round(float(np.percentile(layer_us, 10)), 2),
                 "layer_us_p90": round(float(np.percentile(layer_us, 90)), 2),
                 "tokens_per_s": round(T / med * 1e6, 1),

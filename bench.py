@@ -481,14 +481,37 @@ def cpu_baseline(wl, T, threads, budget_s=10.0, seed=0):
             "timed_s": round(t_route + t_dispatch + t_ffn + t_shared + t_combine, 2)}
 
 
+def source_digest(source):
+    """First 16 hex digits of the SHA-256 of a kernel source file followed by
+    every local header it includes, transitively, each once in include order
+    (looked up in csrc/, then include/)."""
+    dirs = [os.path.join(ROOT, "combine_experts_amd", "csrc"), os.path.join(ROOT, "include")]
+    h, seen = hashlib.sha256(), set()
+
+    def add(name):
+        if name in seen:
+            return
+        seen.add(name)
+        path = next((os.path.join(d, name) for d in dirs if os.path.exists(os.path.join(d, name))), None)
+        if path is None:
+            return
+        text = open(path, "rb").read()
+        h.update(text)
+        for inc in re.findall(rb'^\s*#\s*include\s+"([^"]+)"', text, re.M):
+            add(inc.decode())
+
+    add(source)
+    return h.hexdigest()[:16]
+
+
 def kernel_traffic(key, source):
     """HBM bytes per launch measured with rocprofv3 counters, from the
-    committed summary, if it was taken on the current kernel source."""
+    committed summary, if it was taken on the current kernel source and the
+    headers it includes."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.md")
     if not os.path.exists(path):
         return None
-    src = open(os.path.join(ROOT, "combine_experts_amd", "csrc", source), "rb").read()
-    digest = hashlib.sha256(src).hexdigest()[:16]
+    digest = source_digest(source)
     for line in open(path):
         m = re.match(r"\|\s*" + re.escape(key) + r"\s*\|\s*([0-9a-f]{16})\s*\|\s*([0-9.eE+,]+)\s*\|", line)
         if m and m.group(1) == digest:

@@ -19,6 +19,7 @@ struct Stage {
   Step x[NX][TT];
   i32x4_t xp[XP > 0 ? XP : 1];
   float sx[NX][TT][2]; // E4M3 activation scales of the step's two 128-blocks
+  float xsp[2];        // shared tile: one row's two activation scales, on their way to LDS
   float sw[NMAT][2];   // E4M3 weight block scales of the step
 };
 
@@ -170,7 +171,10 @@ __device__ __forceinline__ void lds_barrier() {
 // their MFMA B operands from the slot.  Needs the same number of K-steps per
 // item on every wave (the launch checks that the K-split divides every
 // item's steps), so that all waves of the workgroup meet the same barriers
-// in the same order.
+// in the same order.  E4M3 walks share the step's activation scales the same
+// way: the first TT*16 lanes of the K-split part load one row's pair each,
+// instead of every wave loading all rows' pairs (a 4- or 8-byte load per
+// row, each a cache-line request of its own).
 //
 // GATHER (the fused layer): the compact-layout offsets [E+1] come from
 // off_src instead of p.expert_offset (the caller routed in LDS), and routed
@@ -197,6 +201,8 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk, 
   __shared__ float red[RED];
   // three stage slots per K-split part, rows XOR-swizzled in 16-byte units
   __shared__ __attribute__((aligned(16))) uint8_t xs[SHARE ? 3 * KS * XT : 16];
+  constexpr bool SSC = SHARE && FP8;  // shared activation scales
+  __shared__ float2 xsc[SSC ? 3 * KS * TT * 16 : 1];
   __shared__ float amax_s[FW][TT * 16];
   __shared__ int s_off[1025];
   __shared__ int s_act[1024];
@@ -291,6 +297,16 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk, 
           s.xp[q] = i32x4_t{(int)v.x, (int)v.y, 0, 0};
         }
       }
+      if constexpr (SSC) {
+        const int i = ft * 64 + lane;  // row of the tile whose scales this lane loads
+        if (i < TT * 16) {
+          int arow = c.it.rows0 + (i < c.it.nrows ? i : 0);  // rows past the group's end: never stored
+          if constexpr (GATHER) arow = c.it.gather ? c.it.gather[arow] : arow;
+          const float* sp = c.it.act_scale + (size_t)arow * (c.it.K / 128) + 2 * ps;
+          s.xsp[0] = sp[0];
+          s.xsp[1] = sp[1];
+        }
+      }
     }
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
@@ -315,7 +331,7 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk, 
         size_t arow = row;
         if constexpr (GATHER) arow = c.it.gather ? (size_t)c.it.gather[row] : row;
         if constexpr (!SHARE) load_step(s.x[xi][tt], c.it.act + arow * rowbytes + (size_t)ps * 256, lane);
-        if constexpr (FP8) {
+        if constexpr (FP8 && !SSC) {
           const float* sp = c.it.act_scale + arow * (c.it.K / 128) + 2 * ps;
           s.sx[xi][tt][0] = sp[0];
           s.sx[xi][tt][1] = sp[1];
@@ -343,6 +359,18 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk, 
         if constexpr (PB == 16) *reinterpret_cast<i32x4_t*>(dst) = s.xp[q];
         else *reinterpret_cast<uint2*>(dst) = make_uint2((unsigned)s.xp[q][0], (unsigned)s.xp[q][1]);
       }
+      if constexpr (SSC) {
+        const int i = ft * 64 + lane;
+        if (i < TT * 16) xsc[(slot * KS + kp) * TT * 16 + i] = make_float2(s.xsp[0], s.xsp[1]);
+      }
+    }
+  };
+  // activation scales of token tile tt's row (lane % 16) at a stage
+  auto xscale = [&](const St& s, int slot, int tt) {
+    if constexpr (SSC) {
+      return xsc[(slot * KS + kp) * TT * 16 + tt * 16 + r16];
+    } else {
+      return make_float2(s.sx[0][tt][0], s.sx[0][tt][1]);
     }
   };
   // activation operand of token tile tt: from the stage, or from LDS slot
@@ -372,7 +400,8 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk, 
           for (int m = 0; m < NMAT; ++m) {
             const f32x4_t p0 = mma_fp8_block(s.w[m], xv, 0);
             const f32x4_t p1 = mma_fp8_block(s.w[m], xv, 1);
-            const float c0 = s.sw[m][0] * s.sx[0][tt][0], c1 = s.sw[m][1] * s.sx[0][tt][1];
+            const float2 sx = xscale(s, slot, tt);
+            const float c0 = s.sw[m][0] * sx.x, c1 = s.sw[m][1] * sx.y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[m][tt][j] += p0[j] * c0 + p1[j] * c1;
           }
@@ -395,7 +424,8 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk, 
             const Step& xv = SHARE ? xb[tt] : s.x[xi][tt];
             const f32x4_t p0 = mma_fp8_block(s.w[m], xv, 0);
             const f32x4_t p1 = mma_fp8_block(s.w[m], xv, 1);
-            const float c0 = sw0 * s.sx[xi][tt][0], c1 = sw1 * s.sx[xi][tt][1];
+            const float2 sx = xscale(s, slot, tt);
+            const float c0 = sw0 * sx.x, c1 = sw1 * sx.y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[m][tt][j] += p0[j] * c0 + p1[j] * c1;
           }

@@ -314,10 +314,15 @@ __device__ __forceinline__ void ffn_body(const FfnParams& p, int bid, int nblk, 
       const int row = (GATED ? (m == 0 ? 0 : c.it.Nout) : 16 * m) + c.it.col0 + r16;
       load_step(s.w[m], c.it.w + (size_t)row * rowbytes + (size_t)ps * 256, lane);
       if constexpr (FP8) {
+        // the block scales are the same for the whole wave and never written
+        // during the launch: scalar loads (constant address space), so the
+        // vector-memory path carries only the tiles
         const int wsrow = ((GATED ? (m == 0 ? 0 : c.it.Nout) : 16 * m) + c.it.col0) / 128;
         const float* wsp = c.it.w_scale + (size_t)wsrow * (c.it.K / 128) + 2 * ps;
-        s.sw[m][0] = wsp[0];
-        s.sw[m][1] = wsp[1];
+        typedef const __attribute__((address_space(4))) float cfloat;
+        const cfloat* q = (const cfloat*)(uintptr_t)wsp;
+        s.sw[m][0] = q[0];
+        s.sw[m][1] = q[1];
       }
     }
 #pragma unroll

@@ -10,9 +10,12 @@ namespace moe {
 
 template <int ACT>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  const int t = blockIdx.x;
-  const int c = (blockIdx.y * 256 + threadIdx.x) * 4;  // first of 4 columns
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  // the column chunks of one token are consecutive workgroups, so the reads
+  // of each expert-output row run in address order
+  const int nch = (p.d / 4 + 255) / 256;
+  const int t = blockIdx.x / nch;
+  const int c = ((blockIdx.x - t * nch) * 256 + threadIdx.x) * 4;  // first of 4 columns
+  if (blockIdx.x == 0)
     for (int e = threadIdx.x; e < p.E; e += 256) p.expert_count[e] = 0;  // ready for the next route
   if (c >= p.d) return;
   const int k = p.k;
@@ -61,7 +64,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-  const dim3 grid(p.T, (p.d / 4 + 255) / 256), block(256);
+  const long long blocks = (long long)p.T * ((p.d / 4 + 255) / 256);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(256);
   if (p.act_dtype == MOE_F32)
     hipLaunchKernelGGL(combine_kernel<MOE_F32>, grid, block, 0, stream, p);
   else

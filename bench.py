@@ -281,9 +281,10 @@ def measure(layer, b, steps, warmup, flush, graph=False):
 
 
 def measure_router(layer, b, wl, steps, flush):
-    """Mean µs of the router GEMM (moe_router_logits: logits = x W_r^T, fp32
-    out) for the batch's tokens, caches flushed before every call.  Reported
-    beside the layer, not inside it: the layer's input is the logits."""
+    """Mean µs of the router GEMM (moe_router_logits_ws: logits = x W_r^T,
+    fp32 out, its reduction split over workgroups where that helps) for the
+    batch's tokens, caches flushed before every call.  Reported beside the
+    layer, not inside it: the layer's input is the logits."""
     import torch
     import moe_inputs as mi
     import combine_experts_amd as M
@@ -293,12 +294,18 @@ def measure_router(layer, b, wl, steps, flush):
         wr = mi.gen_router_weight(wl)
         layer.w_router = torch.from_numpy(wr.view(np.int16) if wr.dtype == np.uint16 else wr).cuda()
     out = torch.empty((b.T, wl.num_experts), dtype=torch.float32, device="cuda")
-    M.moe_router_logits(layer.cfg, b.T, b.x, layer.w_router, out)
+    nb = M.moe_router_workspace_size(layer.cfg, b.T)
+    rws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+
+    def call():
+        M.moe_router_logits_ws(layer.cfg, b.T, b.x, layer.w_router, out, rws, nb)
+
+    call()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for s_, e_ in ev:
         flush()
         s_.record()
-        M.moe_router_logits(layer.cfg, b.T, b.x, layer.w_router, out)
+        call()
         e_.record()
     torch.cuda.synchronize()
     return float(np.mean([s_.elapsed_time(e_) * 1e3 for s_, e_ in ev]))

@@ -11,7 +11,7 @@ from ._binding import (  # noqa: F401
     moe_combine, moe_dispatch, moe_dispatch_rows, moe_expert_ffn, moe_ffn_down, moe_ffn_gate_up,
     moe_ffn_workspace_size, moe_fused_supported, moe_fused_workspace_size, moe_layer, moe_layer_fused,
     moe_layer_static, moe_layer_static_max_bytes,
-    moe_router_logits,
+    moe_router_logits, moe_router_logits_ws, moe_router_workspace_size,
     moe_route, moe_route_dispatch, moe_status_string, moe_workspace_size)
 
 load_library()

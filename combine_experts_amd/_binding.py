@@ -75,6 +75,9 @@ def load_library():
     lib.moe_combine.argtypes = [cp, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_layer.argtypes = [cp, i32, vp, vp, vp, wp, vp, vp, sz, vp]
     lib.moe_router_logits.argtypes = [cp, i32, vp, vp, vp, vp]
+    lib.moe_router_logits_ws.argtypes = [cp, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_router_workspace_size.argtypes = [cp, i32]
+    lib.moe_router_workspace_size.restype = sz
     lib.moe_layer_fused.argtypes = [cp, i32, vp, vp, vp, vp, wp, vp, vp, sz, vp]
     lib.moe_fused_workspace_size.argtypes = [cp, i32]
     lib.moe_fused_workspace_size.restype = sz
@@ -84,7 +87,7 @@ def load_library():
     lib.moe_layer_static_max_bytes.argtypes = []
     lib.moe_layer_static_max_bytes.restype = sz
     for f in (lib.moe_layer_fused, lib.moe_layer_static, lib.moe_route, lib.moe_dispatch, lib.moe_route_dispatch, lib.moe_expert_ffn, lib.moe_ffn_gate_up,
-              lib.moe_ffn_down, lib.moe_combine, lib.moe_layer, lib.moe_router_logits):
+              lib.moe_ffn_down, lib.moe_combine, lib.moe_layer, lib.moe_router_logits, lib.moe_router_logits_ws):
         f.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -195,6 +198,15 @@ def moe_layer(cfg, T, x, logits, bias, weights: MoeWeights, y, ws, ws_bytes, str
 def moe_router_logits(cfg, T, x, w_router, logits, stream=None):
     _check(load_library().moe_router_logits(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logits),
                                             _stream(stream)))
+
+
+def moe_router_logits_ws(cfg, T, x, w_router, logits, ws, ws_bytes, stream=None):
+    _check(load_library().moe_router_logits_ws(ctypes.byref(cfg), T, _ptr(x), _ptr(w_router), _ptr(logits),
+                                               _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def moe_router_workspace_size(cfg: MoeConfig, max_tokens: int) -> int:
+    return load_library().moe_router_workspace_size(ctypes.byref(cfg), max_tokens)
 
 
 def moe_layer_static(cfg, T, x, logits, bias, weights: MoeWeights, y, stream=None):

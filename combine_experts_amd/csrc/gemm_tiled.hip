@@ -62,6 +62,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 struct TItem {
   int valid, rows0, nrows, K, Nout, f0, m0;
+  int s0, S;  // the item's K-steps: [s0, s0 + S)
   const uint8_t* w;
   const uint8_t* act;
   void* out;
@@ -149,11 +150,14 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
   const int routed_items = __builtin_amdgcn_readfirstlane(s_pre[n_active]);
   const int shared_mt = p.n_shared ? (p.T + BN - 1) / BN : 0;
   const int n_items = routed_items + shared_mt * nt_s;
+  // split reduction (router GEMM only): item q * n_items + i is part q of tile i
+  const int ksp = p.ksplit > 1 ? p.ksplit : 1;
 
-  auto decode = [&](int item) {
+  auto decode = [&](int item_all) {
     TItem it{};
-    it.valid = item < n_items;
+    it.valid = item_all < n_items * ksp;
     if (!it.valid) return it;
+    const int part = item_all / n_items, item = item_all - part * n_items;
     int local, mt;
     if (item < routed_items) {
       // binary search: last active group a with s_pre[a] <= item
@@ -188,6 +192,10 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
     // token tile fastest: consecutive items share one weight tile
     it.m0 = (local % mt) * BN;
     it.f0 = (local / mt) * fcols;
+    const int steps = it.K / BK;
+    it.s0 = part * steps / ksp;
+    it.S = (part + 1) * steps / ksp - it.s0;
+    if (ksp > 1) it.out = static_cast<float*>(it.out) + (size_t)part * p.T * it.Nout;
     return it;
   };
 
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
   // below hold on every path.
   auto issue = [&](const TItem& it, int s, int S, uint8_t* wb, uint8_t* tb) {
     const bool real = s < S;
-    const size_t kb = (size_t)s * ROWB;
+    const size_t kb = (size_t)(it.s0 + s) * ROWB;
 #pragma unroll
     for (int q = 0; q < WPW; ++q) dma16(real ? gw[q] + kb : it.w, wb + 1024 * (wid * WPW + q));
 #pragma unroll
@@ -310,11 +318,12 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
   const int nx = gridDim.x % 8 == 0 ? 8 : 1;
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
   const int per_x = gridDim.x / nx;
-  const int span = (n_items + nx - 1) / nx;
-  const int lo_x = xcd * span, hi_x = min(n_items, lo_x + span);
+  const int n_all = n_items * ksp;
+  const int span = (n_all + nx - 1) / nx;
+  const int lo_x = xcd * span, hi_x = min(n_all, lo_x + span);
   for (int item = lo_x + slot; item < hi_x; item += per_x) {
     const TItem it = decode(item);
-    const int S = it.K / BK;
+    const int S = it.S;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -351,8 +360,9 @@ __global__ __launch_bounds__(2 * WR) void gemm_tiled_kernel(FfnParams p) {
 template <bool GATED, int WR>
 static hipError_t launch_wr(const FfnParams& p, long long max_token_tiles, hipStream_t stream) {
   constexpr int fcols = GATED ? WR / 2 : WR;
-  const long long max_items = max_token_tiles * (p.Nout_r / fcols) +
-                              (p.n_shared ? (long long)((p.T + BN - 1) / BN) * (p.Nout_s / fcols) : 0);
+  const long long max_items = (max_token_tiles * (p.Nout_r / fcols) +
+                               (p.n_shared ? (long long)((p.T + BN - 1) / BN) * (p.Nout_s / fcols) : 0)) *
+                              (p.ksplit > 1 ? p.ksplit : 1);
   auto kern = gemm_tiled_kernel<GATED, WR>;
   // constant per kernel and device model: computed once (thread-safe
   // initialisation of a const local static)

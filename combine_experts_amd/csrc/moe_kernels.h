@@ -69,6 +69,10 @@ struct FfnParams {
   int K_s, NW_s, Nout_s;
   void* s_out;
   float* s_out_scale;
+  // LDS-tiled plain pass with no routed groups only (the router GEMM): the
+  // reduction is split into ksplit parts (<= 1: not split); part q writes its
+  // fp32 partial sums to s_out + q * T * Nout_s
+  int ksplit;
 };
 
 struct CombineParams {
@@ -156,6 +160,8 @@ hipError_t launch_router_gemm(const FfnParams& p, int dtype, hipStream_t stream)
 bool router_gemv_fits(int T, int d, int dtype);
 hipError_t launch_router_gemv(const void* x, const void* w, float* logits, int T, int E, int d, int dtype,
                               hipStream_t stream);
+// logits[i] = sum of part[q][i] over q = 0 .. P-1 in that order (n values, n % 4 == 0)
+hipError_t launch_router_split_sum(const float* part, float* logits, long long n, int P, hipStream_t stream);
 
 // FfnParams::tiles_r / tiles_s count 16-column tiles; launch_ffn groups them
 // into the work items of the launch shape it picks (a gated E4M3 pass always

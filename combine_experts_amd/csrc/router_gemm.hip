@@ -62,4 +62,28 @@ hipError_t launch_router_gemv(const void* x, const void* w, float* logits, int T
   return hipErrorInvalidValue;
 }
 
+// The split router GEMM's partial sums -> logits: logits[i] = sum over the
+// parts q = 0 .. P-1 of part[q][i], added in that order (fp32), four values
+// per thread.
+__global__ __launch_bounds__(256) void router_split_sum_kernel(const float* __restrict__ part, float* logits,
+                                                               long long n, int P) {
+  const long long i = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t*>(part + i);
+  for (int q = 1; q < P; ++q) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + (size_t)q * n + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] += v[j];
+  }
+  *reinterpret_cast<f32x4_t*>(logits + i) = acc;
+}
+
+hipError_t launch_router_split_sum(const float* part, float* logits, long long n, int P, hipStream_t stream) {
+  if (n <= 0 || n % 4 || P < 1) return hipErrorInvalidValue;
+  const long long blocks = (n / 4 + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(router_split_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, logits, n, P);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -280,10 +280,33 @@ moe_status moe_combine(const moe_config* cfg, int32_t T, const float* expert_out
  *   logits   [T][E] fp32, written.
  * The products are exact in fp32 and are summed in fp32 in a fixed order, so
  * the result is reproducible run to run.  Requires E % 64 == 0
- * (MOE_ERR_UNSUPPORTED otherwise).  Needs no workspace.
+ * (MOE_ERR_UNSUPPORTED otherwise).  Needs no workspace (moe_router_logits_ws,
+ * below, takes one to run larger batches faster).
  */
 moe_status moe_router_logits(const moe_config* cfg, int32_t T, const void* x, const void* w_router,
                              float* logits, void* stream);
+
+/*
+ * moe_router_logits_ws: moe_router_logits with a caller workspace, which lets
+ * the product's reduction (the sum over c) be split over workgroups where
+ * moe_router_logits would leave most of the GPU idle: bf16 layers with
+ * E % 128 == 0, from 256 tokens on when d_model >= 4096, else from 1024.  Each of P parts sums its share of c in fp32
+ * into ws, and a second launch adds the P partial sums in part order, so the
+ * result is reproducible run to run; it may differ from moe_router_logits'
+ * in the last bits (another summation order).  Elsewhere the call is
+ * moe_router_logits and ws is not touched.
+ *   x, w_router, logits: as for moe_router_logits.
+ *   ws, ws_bytes: at least moe_router_workspace_size(cfg, T) bytes, 16-byte
+ *   aligned, no initial contents needed (scratch, overwritten); may be NULL
+ *   when that size is 0.  MOE_ERR_WORKSPACE_TOO_SMALL when ws_bytes is
+ *   smaller, nothing launched.
+ */
+moe_status moe_router_logits_ws(const moe_config* cfg, int32_t T, const void* x, const void* w_router,
+                                float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of workspace moe_router_logits_ws needs for any T <= max_tokens (0:
+ * it splits nothing there).  0 for an invalid cfg or max_tokens < 0. */
+size_t moe_router_workspace_size(const moe_config* cfg, int32_t max_tokens);
 
 /*
  * moe_layer: route -> dispatch -> expert FFN (+ shared expert) -> combine in

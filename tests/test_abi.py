@@ -164,6 +164,50 @@ def test_router_logits_argument_checks(M):
     assert e.value.status == M.MOE_ERR_UNSUPPORTED
 
 
+def split_parts(T, E, d):
+    """Parts of the router GEMM's reduction in moe_router_logits_ws: bf16,
+    E % 128 == 0, from 256 tokens (d >= 4096) or 1024; ~256 items of 128
+    tokens x WR experts (WR 256 when E % 256 == 0, else 128), at most 16
+    parts of at least 8 K-steps of 64."""
+    if E % 128 or T < (256 if d >= 4096 else 1024):
+        return 1
+    tiles = -(-T // 128) * (E // (256 if E % 256 == 0 else 128))
+    P = min(16, 256 // tiles, d // 64 // 8)
+    return P if P >= 2 else 1
+
+
+def test_router_split_workspace(M):
+    """moe_router_workspace_size is the largest P T E 4 bytes over the token
+    counts up to max_tokens; too small or misaligned workspaces are refused
+    before anything is launched."""
+    cfg = dsv3(M)  # E 256, d 7168: 112 K-steps, so P <= 14
+
+    def size(maxT, E=256, d=7168):
+        best = 0
+        for T in range(1, maxT + 1):
+            P = split_parts(T, E, d)
+            best = max(best, P * T * E * 4 if P > 1 else 0)
+        return best
+
+    assert M.moe_router_workspace_size(cfg, 255) == 0
+    for maxT in (256, 300, 2048, 4096, 4100, 20000):
+        assert M.moe_router_workspace_size(cfg, maxT) == size(maxT), maxT
+    assert M.moe_router_workspace_size(cfg, 4096) == 8 * 4096 * 256 * 4
+    q = dsv3(M, num_experts=128, d_model=2048, n_group=8, topk_group=4)  # d 2048: P <= 4, from 1024 tokens
+    assert M.moe_router_workspace_size(q, 1023) == 0
+    for maxT in (1024, 2048, 5000):
+        assert M.moe_router_workspace_size(q, maxT) == size(maxT, 128, 2048), maxT
+    assert M.moe_router_workspace_size(dsv3(M, act_dtype="f32", weight_dtype="f32"), 4096) == 0
+    assert M.moe_router_workspace_size(dsv3(M, num_experts=64, n_group=8, topk_group=4), 4096) == 0
+    with pytest.raises(M.MoeError) as e:
+        M.moe_router_logits_ws(cfg, 4096, 16, 16, 16, 16, 8 * 4096 * 256 * 4 - 1, stream=0)
+    assert e.value.status == M.MOE_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(M.MoeError) as e:  # misaligned workspace
+        M.moe_router_logits_ws(cfg, 4096, 16, 16, 16, 24, 8 * 4096 * 256 * 4, stream=0)
+    assert e.value.status == M.MOE_ERR_INVALID_ARG
+    M.moe_router_logits_ws(cfg, 0, None, None, None, None, 0, stream=0)  # T = 0: nothing to do
+
+
 def test_fused_layer_support_and_argument_checks(M):
     """moe_layer_fused covers bf16 layers of 1-16 tokens with up to 256
     experts, and rejects everything else before launching."""

@@ -47,14 +47,47 @@ def test_router_logits(name, T):
     import combine_experts_amd as M
     say(f"\n[gpu-test] router logits {name} T={T}")
     wl = CASES[name]
-    E = wl.num_experts
-    x = mi.gen_x(wl, T)
-    wr = mi.gen_router_weight(wl)
+    x, wr = mi.gen_x(wl, T), mi.gen_router_weight(wl)
     xd, wd = dev(x), dev(wr)
+    run = lambda out: M.moe_router_logits(cfg_of(wl), T, xd, wd, out)
+    _check_logits(wl, T, x, wr, run)
+
+
+@pytest.mark.parametrize("name,T", [("dsv3_prefill", 4096), ("dsv3", 2048), ("dsv3", 2176), ("dsv3", 300),
+                                    ("dsv3", 256), ("qwen3", 1024), ("qwen3", 2048), ("qwen3", 4100),
+                                    ("bf16_64", 2048), ("qwen3", 300), ("dsv3", 255), ("dsv3", 16)])
+def test_router_logits_split(name, T):
+    """moe_router_logits_ws: the reduction split over workgroups into fp32
+    partial sums, added in part order by a second launch (bf16, E % 128 ==
+    0, from 256 tokens when d_model >= 4096, else from 1024; elsewhere it is
+    moe_router_logits).  The same bound
+    against the oracle, reproducible bits, a workspace poisoned with NaN
+    first (every partial is written before it is read)."""
+    import combine_experts_amd as M
+    say(f"\n[gpu-test] split router logits {name} T={T}")
+    wl = CASES[name]
+    cfg = cfg_of(wl)
+    nb = M.moe_router_workspace_size(cfg, T)
+    split = wl.num_experts % 128 == 0 and T >= (256 if wl.d_model >= 4096 else 1024)
+    assert (nb > 0) == split
+    ws = torch.full((max(nb, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    x, wr = mi.gen_x(wl, T), mi.gen_router_weight(wl)
+    xd, wd = dev(x), dev(wr)
+    run = lambda out: M.moe_router_logits_ws(cfg, T, xd, wd, out, ws if nb else None, nb)
+    got = _check_logits(wl, T, x, wr, run)
+    if not split:  # the call is moe_router_logits
+        plain = torch.empty_like(got)
+        M.moe_router_logits(cfg, T, xd, wd, plain)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(plain).view(np.uint32), host(got).view(np.uint32))
+
+
+def _check_logits(wl, T, x, wr, run):
+    E = wl.num_experts
     out = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
-    M.moe_router_logits(cfg_of(wl), T, xd, wd, out)
+    run(out)
     again = torch.full_like(out, float("nan"))
-    M.moe_router_logits(cfg_of(wl), T, xd, wd, again)
+    run(again)
     torch.cuda.synchronize()
     got = host(out).astype(np.float64)
     assert np.array_equal(host(out).view(np.uint32), host(again).view(np.uint32)), "not reproducible"
@@ -77,3 +110,4 @@ def test_router_logits(name, T):
     assert not (differ & ~(margin <= slack)).any()
     say(f"  max |err| / bound = {float((err / bound).max()):.3f}, max |err| = {float(err.max()):.2e}, "
         f"{int(differ.sum())} of {T} tokens route differently (all near ties)")
+    return out

@@ -145,3 +145,47 @@ def test_graph_router_gemm_then_layer(T):
             assert np.array_equal(host(y), want[i]), (rep, i)
             (torch.randn(1 << 16, device="cuda") * 2).sum().item()
     say(f"  router GEMM + layer T={T}: 6 replays equal the eager calls")
+
+
+def test_graph_split_router_gemm():
+    """moe_router_logits_ws with its reduction split (two launches: partial
+    sums, then their sum in part order) captured once: every replay on new
+    tokens equals the eager call bit for bit."""
+    import combine_experts_amd as M
+    from moe_case import dev
+    say("\n[gpu-test] graph split router GEMM")
+    wl = WL["dsv3"].with_(name="router_split_graph", num_experts=128, top_k=4, d_model=4096, d_ff=256,
+                          d_ff_shared=0, num_shared=0, n_group=4, topk_group=2)
+    cfg = cfg_of(wl)
+    T = 256
+    nb = M.moe_router_workspace_size(cfg, T)
+    assert nb > 0  # 256 tokens at d_model 4096 take the split
+    wr = dev(mi.gen_router_weight(wl))
+    xs = [dev(mi.gen_x(wl, T, seed=s)) for s in (31, 32, 33)]
+    ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+
+    def eager(x):
+        out = torch.full((T, wl.num_experts), float("nan"), dtype=torch.float32, device="cuda")
+        M.moe_router_logits_ws(cfg, T, x, wr, out, ws, nb)
+        torch.cuda.synchronize()
+        return host(out)
+
+    want = [eager(x) for x in xs]
+    x = xs[0].clone()
+    out = torch.empty((T, wl.num_experts), dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            M.moe_router_logits_ws(cfg, T, x, wr, out, ws, nb)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, xi in enumerate(xs):
+            x.copy_(xi)
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(host(out).view(np.uint32), want[i].view(np.uint32)), (rep, i)
+            (torch.randn(1 << 16, device="cuda") * 2).sum().item()
+    say("  split router GEMM: 6 replays equal the eager calls")

@@ -126,13 +126,15 @@ hipError_t launch_ffn(const FfnParams& p, int wdtype, bool gated, long long rout
   const int step = wdtype == MOE_F32 ? 64 : wdtype == MOE_BF16 ? 128 : 256;
   if (p.K_r / step < 1 || (p.n_shared && p.K_s / step < 1)) return hipErrorInvalidValue;
   Plan pl = plan_of(p, step, gated, wdtype);
-  // E4M3 batches with many rows per expert (T k >= 12 E) use 32-row chunks:
-  // each weight tile is then streamed once per 32 rows instead of once per 16
-  // (measured at 512 tokens x 8 of 256 experts: gate/up 2036 -> 1792 us; at
-  // 128 tokens the 16-row chunks are faster).  The wider activation tiles
-  // leave no registers for parked accumulators, so those walks finish each
-  // item in line.
-  const bool wide = wdtype == MOE_FP8_E4M3 && routed_rows >= 12LL * max_groups;
+  // E4M3 batches with at least one row per expert on average (T k >= E) use
+  // wide chunks (64 rows where the launch shape allows, below; else 32): each
+  // weight tile is then streamed once per 64 rows instead of once per 16.  The
+  // wider activation tiles leave no registers for parked accumulators, so
+  // those walks finish each item in line.  Measured layer us against 16-row
+  // chunks, 8 of 256 experts, two runs each on one box: 16 tokens 690 / 685
+  // (below the rule), 32 964 / 1007, 48 1092 / 1131, 64 1184 / 1168, 80 1213 /
+  // 1250, 96 1314 / 1363, 128 1426 / 1449, 256 1589 / 1780.
+  const bool wide = wdtype == MOE_FP8_E4M3 && p.E > 0 && routed_rows >= p.E;
   // Once experts hold a few rows each, the E4M3 down pass does better with
   // more column waves sharing each activation tile and no K-split.  Measured
   // at 256 experts x 8 slots, down pass with (2, 2) / (4, 1) / (8, 1): 512

@@ -488,10 +488,20 @@ def cpu_baseline(wl, T, threads, budget_s=10.0, seed=0):
             "timed_s": round(t_route + t_dispatch + t_ffn + t_shared + t_combine, 2)}
 
 
+def _code_only(text):
+    """Source text without its // and /* */ comments (string literals in
+    these sources hold no comment markers), blank lines and the spaces that
+    begin or end a line, so that editing a comment or the layout does not
+    change a kernel's key."""
+    text = re.sub(rb"/\*.*?\*/", b"", text, flags=re.S)
+    text = re.sub(rb"//[^\n]*", b"", text)
+    return b"\n".join(line.strip() for line in text.splitlines() if line.strip())
+
+
 def source_digest(source):
     """First 16 hex digits of the SHA-256 of a kernel source file followed by
     every local header it includes, transitively, each once in include order
-    (looked up in csrc/, then include/)."""
+    (looked up in csrc/, then include/), comments removed."""
     dirs = [os.path.join(ROOT, "combine_experts_amd", "csrc"), os.path.join(ROOT, "include")]
     h, seen = hashlib.sha256(), set()
 
@@ -503,7 +513,7 @@ def source_digest(source):
         if path is None:
             return
         text = open(path, "rb").read()
-        h.update(text)
+        h.update(_code_only(text))
         for inc in re.findall(rb'^\s*#\s*include\s+"([^"]+)"', text, re.M):
             add(inc.decode())
 

@@ -23,6 +23,12 @@
 // feature tile, token tile), token tile fastest, and each XCD walks a
 // contiguous range of them, so the workgroups running at the same time on
 // one XCD share a hot expert's weight tile through that XCD's L2.
+//
+// The plain pass also serves the router GEMM for large batches (one group of
+// all T tokens, fp32 out).  There it has only ceil(T/128) x E/WR tiles, so
+// with a workspace the K-steps can be split into parts (FfnParams::ksplit):
+// item q n + i is part q of tile i, and part q writes its fp32 partial sums
+// to its own slice of the output; a second launch adds the parts in order.
 #include "moe_kernels.h"
 
 namespace moe {

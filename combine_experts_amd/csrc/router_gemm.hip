@@ -10,6 +10,10 @@
 // every token (fused multiply-adds in a fixed order), then the lanes reduce
 // with a fixed shuffle tree and the four waves add their sums through LDS in
 // wave order.  The result is reproducible run to run.
+//
+// The file also holds the second launch of the split router GEMM (larger
+// batches, LDS-tiled kernel with its reduction in parts): the sum of the
+// parts' fp32 partial sums in part order.
 #include "router_gemv.h"
 
 namespace moe {

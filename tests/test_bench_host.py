@@ -19,25 +19,31 @@ def _tree(tmp_path):
     return tmp_path
 
 
-def test_source_digest_covers_included_headers(tmp_path, monkeypatch):
+def test_source_digest_covers_included_headers_not_comments(tmp_path, monkeypatch):
     root = _tree(tmp_path)
     monkeypatch.setattr(bench, "ROOT", str(root))
     base = {f: bench.source_digest(f) for f in ("gemm_tiled.hip", "ffn.hip")}
     assert base == {f: bench.source_digest(f) for f in base}  # deterministic
     csrc = root / "combine_experts_amd" / "csrc"
-    # a header only ffn.hip includes (through ffn_body.h) changes its key alone
+    # comments, blank lines and indentation do not change a key
     with open(csrc / "ffn_body.h", "a") as fh:
-        fh.write("\n// edited\n")
+        fh.write("\n// a comment\n/* another\n   comment */\n\n   \n")
+    with open(csrc / "gemm_tiled.hip", "a") as fh:
+        fh.write("\n\n  // a comment\n")
+    assert {f: bench.source_digest(f) for f in base} == base
+    # code in a header only ffn.hip includes (through ffn_body.h) changes its key alone
+    with open(csrc / "ffn_body.h", "a") as fh:
+        fh.write("\nstatic const int edited_marker = 1;\n")
     assert bench.source_digest("ffn.hip") != base["ffn.hip"]
     assert bench.source_digest("gemm_tiled.hip") == base["gemm_tiled.hip"]
     # the public header, included by both through moe_kernels.h / moe_device.h
     with open(root / "include" / "moe.h", "a") as fh:
-        fh.write("\n/* edited */\n")
+        fh.write("\ntypedef int edited_marker_t;\n")
     assert bench.source_digest("gemm_tiled.hip") != base["gemm_tiled.hip"]
     # a source neither includes changes neither key
     before = bench.source_digest("gemm_tiled.hip")
     with open(csrc / "combine.hip", "a") as fh:
-        fh.write("\n// edited\n")
+        fh.write("\nstatic const int edited_marker = 2;\n")
     assert bench.source_digest("gemm_tiled.hip") == before
 
 

@@ -98,7 +98,8 @@ hipError_t launch_route(const RouteParams& p, hipStream_t stream) {
 // Grid (T, column blocks).  Compact layout: rows follow from the offsets
 // scan; masked layout: row = expert * T + ticket, no scan.  Plain rows: a
 // block copies 4096 bytes of its token (256 threads x 16 B); E4M3 rows: a
-// block quantises four 128-column blocks (one per wave).  The token's bytes
+// block quantises eight 128-column blocks, two per wave (each half-wave
+// holds one block, four values per lane).  The token's bytes
 // and its slot tickets are loaded before the offsets scan so that their
 // latency overlaps it.
 template <int ACT, bool QUANT>
@@ -116,20 +117,21 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
     my_ticket = p.ticket[o];
   }
   constexpr int EB = Elem<ACT>::kBytes;
-  // plain: this thread's 16-byte piece; E4M3: this lane's two values of the
-  // wave's 128-column block
+  // plain: this thread's 16-byte piece; E4M3: this lane's four values of
+  // its half-wave's 128-column block
   const int piece = blockIdx.y * 256 + tid;
   const int pieces = d * EB / 16;
   const int nb = d / 128;
-  const int blk = blockIdx.y * 4 + wid;
+  const int blk = blockIdx.y * 8 + wid * 2 + (lane >> 5);
+  const int hl = lane & 31;  // lane within the half-wave
   i32x4_t v{};
-  uint32_t pair = 0;
+  uint2 quad{0u, 0u};
   if constexpr (!QUANT) {
     if (piece < pieces)
       v = reinterpret_cast<const i32x4_t*>(static_cast<const uint8_t*>(p.x) + (size_t)t * d * EB)[piece];
   } else {
     if (blk < nb)
-      pair = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.x) + (size_t)t * d)[blk * 64 + lane];
+      quad = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.x) + (size_t)t * d)[blk * 32 + hl];
   }
   if (!p.masked) {  // uniform: the scan's barriers are met by every thread
     block_offsets(p.expert_count, p.E, off, wsum);
@@ -154,19 +156,22 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
         if (rows[j] >= 0)
           reinterpret_cast<i32x4_t*>(static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d * EB)[piece] = v;
   } else {
-    if (blk < nb) {  // uniform per wave
-      const float v0 = bf16_bits_to_f32(pair & 0xFFFFu), v1 = bf16_bits_to_f32(pair >> 16);
-      float amax = fmaxf(fabsf(v0), fabsf(v1));
+    // the block's amax over its half-wave (both halves shuffle together; a
+    // half past the last block holds zeros and stores nothing)
+    const float v0 = bf16_bits_to_f32(quad.x & 0xFFFFu), v1 = bf16_bits_to_f32(quad.x >> 16);
+    const float v2 = bf16_bits_to_f32(quad.y & 0xFFFFu), v3 = bf16_bits_to_f32(quad.y >> 16);
+    float amax = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if (blk < nb) {
       const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-      const uint32_t c0 = f32_to_e4m3(v0 / scale), c1 = f32_to_e4m3(v1 / scale);
-      const uint16_t codes = (uint16_t)(c0 | (c1 << 8));
+      const uint32_t codes = f32_to_e4m3(v0 / scale) | (f32_to_e4m3(v1 / scale) << 8) |
+                             (f32_to_e4m3(v2 / scale) << 16) | (f32_to_e4m3(v3 / scale) << 24);
       for (int j = 0; j < nrows; ++j) {
         if (rows[j] < 0) continue;
         uint8_t* dst = static_cast<uint8_t*>(p.recv) + (size_t)rows[j] * d;
-        reinterpret_cast<uint16_t*>(dst + blk * 128)[lane] = codes;
-        if (lane == 0) p.recv_scale[(size_t)rows[j] * nb + blk] = scale;
+        reinterpret_cast<uint32_t*>(dst + blk * 128)[hl] = codes;
+        if (hl == 0) p.recv_scale[(size_t)rows[j] * nb + blk] = scale;
       }
     }
   }
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchParams p) {
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t stream) {
   const dim3 block(256);
   if (p.quant) {
-    const dim3 grid(p.T, (p.d / 128 + 3) / 4);
+    const dim3 grid(p.T, (p.d / 128 + 7) / 8);
     hipLaunchKernelGGL((dispatch_kernel<MOE_BF16, true>), grid, block, 0, stream, p);
   } else if (p.act_dtype == MOE_F32) {
     const dim3 grid(p.T, (p.d * 4 / 16 + 255) / 256);

@@ -152,7 +152,9 @@ SMALL_LAYER = [("tiny", 16), ("tiny", 1), ("tiny", 17), ("tiny", 129), ("qwen3",
                ("tiled_small", 129), ("tiled_small", 1100), ("tiled_narrow", 257), ("qwen3", 512),
                ("fp8_rows", 200), ("fp8_rows", 67), ("cosched", 1), ("cosched", 45), ("cosched", 60),
                ("qwen3", 256),
-               ("share_odd", 40), ("fp8_odd", 3), ("fp8_odd", 40)]
+               ("share_odd", 40), ("fp8_odd", 3), ("fp8_odd", 40),
+               # either side of the E4M3 wide-chunk rule (T k >= E: 64-row chunks): 32 experts x 4
+               ("fp8_small", 8), ("fp8_small", 7)]
 
 
 @pytest.mark.parametrize("name,T", SMALL_LAYER)

@@ -30,6 +30,8 @@ CASES = {
     # bf16, 64 experts: many tokens still take the streaming kernel (the tiled
     # one needs E % 128 == 0)
     "bf16_64": WL["qwen3"].with_(name="bf16_64", num_experts=64, top_k=4),
+    # 512 experts: two 256-wide expert tiles per token tile in the tiled and split passes
+    "e512": WL["dsv3"].with_(name="e512", num_experts=512, n_group=8, topk_group=4),
 }
 
 
@@ -55,7 +57,8 @@ def test_router_logits(name, T):
 
 @pytest.mark.parametrize("name,T", [("dsv3_prefill", 4096), ("dsv3", 2048), ("dsv3", 2176), ("dsv3", 300),
                                     ("dsv3", 256), ("qwen3", 1024), ("qwen3", 2048), ("qwen3", 4100),
-                                    ("bf16_64", 2048), ("qwen3", 300), ("dsv3", 255), ("dsv3", 16)])
+                                    ("bf16_64", 2048), ("qwen3", 300), ("dsv3", 255), ("dsv3", 16),
+                                    ("e512", 512), ("e512", 2100)])
 def test_router_logits_split(name, T):
     """moe_router_logits_ws: the reduction split over workgroups into fp32
     partial sums, added in part order by a second launch (bf16, E % 128 ==
